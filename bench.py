@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for libpagedattn on one MI355X.
+
+One step = the whole hot path over one batch: store_kvcache of the step's new
+token per sequence, then paged_attention_decode (attention kernel plus, when
+contexts are split, the merge kernel). Inputs are seeded synthetic data of the
+workload's shape, resident in HBM before timing starts.
+
+Prints ONE JSON line:
+  value        KV GB/s: logical K+V bytes one decode must read (sum over
+               sequences of L * Hkv * D * 2 bytes * 2) / wall time per step
+  tokens_per_s sequences advanced per second (B / time per step)
+  roofline     the attention kernel alone: the same KV bytes / its mean
+               duration from HIP events recorded on its stream, against
+               MI355X's 8 TB/s HBM peak; traffic from committed rocprofv3
+               counter summaries when they match the current kernel source
+  cpu_baseline the float64 CPU oracle timed on this host on a bounded sample
+               of the same workload (a reported baseline, not the target)
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "paged-attn decode KV HBM GB/s (% of MI355X peak) and decode tokens/s"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "skewed_prefix_bf16"
+KERNEL_SOURCE = ROOT / "paged_attention_decode_amd" / "csrc" / "decode.hip"
+PROFILES = ROOT / "profiles"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=0, help="0 balanced split, -1 one pass, >0 fixed")
+    ap.add_argument("--cold-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush each")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="target seconds of oracle work")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+
+
+def traffic_from_profiles(workload: str, launches_bytes: float):
+    """HBM bytes per launch of the attention kernel from committed counter summaries, or None."""
+    path = PROFILES / f"decode_{workload}_traffic.txt"
+    if not path.exists():
+        return None
+    fields = {}
+    for line in path.read_text().splitlines():
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def describe(cfg) -> dict:
+    lens = {"list": f"{list(cfg.len_list)}", "fixed": f"all {cfg.len_hi}",
+            "uniform": f"uniform [{cfg.len_lo}, {cfg.len_hi}]",
+            "lognormal": f"lognormal median {cfg.len_median:g} sigma {cfg.len_sigma:g} clipped [{cfg.len_lo}, {cfg.len_hi}]"}
+    d = {"workload": cfg.name, "batch": cfg.batch, "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads,
+         "head_dim": cfg.head_dim, "block_size": cfg.block_size, "context_lens": lens[cfg.lengths],
+         "scale": cfg.softmax_scale}
+    if cfg.prefix_group:
+        d["prefix_sharing"] = f"groups of {cfg.prefix_group} sequences share their first {cfg.prefix_tokens} tokens"
+    if cfg.q_mult != 1.0:
+        d["q_scale"] = cfg.q_mult
+    return d
+
+
+def cpu_baseline(x, gpu_out, budget_s: float) -> dict:
+    """Time the float64 oracle on a bounded sample of the batch and compare it with the GPU output."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    c = x.cfg
+    geo = oracle.CacheGeometry(x.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.dtype)
+    k2, v2 = oracle.store_kvcache(x.k_new, x.v_new, x.slot_mapping, x.k_cache, x.v_cache, geo)
+    # pick sequences in a seeded order until the estimated work fills the budget
+    order = np.random.default_rng(12345).permutation(c.batch)
+    probe = order[:1].tolist()
+    t = time.perf_counter()
+    oracle.decode(x.q, k2, v2, x.block_tables, x.context_lens, x.scale, geo, seqs=probe)
+    per_token = (time.perf_counter() - t) / max(1, int(x.context_lens[probe].sum()))
+    seqs, tokens = [], 0
+    for s in order:
+        seqs.append(int(s))
+        tokens += int(x.context_lens[s])
+        if tokens * per_token >= budget_s:
+            break
+    t = time.perf_counter()
+    ref = oracle.decode(x.q, k2, v2, x.block_tables, x.context_lens, x.scale, geo, seqs=seqs)
+    dt = time.perf_counter() - t
+    kv = tokens * c.num_kv_heads * c.head_dim * c.elem_bytes * 2
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    err = float(np.abs(gpu_out[seqs] - ref[seqs]).max())
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(seqs)} of {c.batch} sequences ({tokens} context tokens), float64 numpy, one pass",
+            "seconds": dt, "tokens_per_s": len(seqs) / dt, "host_cpus": len(os.sched_getaffinity(0)),
+            "parity_max_abs_err_vs_gpu": err}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the decode "
+              "path has no cross-GPU step in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_amd as pa
+    from workloads import get_config, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pa.load_library()
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.workload)
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    x = make_inputs(cfg)
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    k_cache = up(x.k_cache).view(pa.k_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, tdt))
+    v_cache = up(x.v_cache).view(pa.v_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size))
+    q, k_new, v_new = up(x.q), up(x.k_new), up(x.v_new)
+    block_tables = torch.from_numpy(x.block_tables).to(dev)
+    context_lens = torch.from_numpy(x.context_lens).to(dev)
+    slots = torch.from_numpy(x.slot_mapping).to(dev)
+    out = torch.empty((cfg.batch, cfg.num_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    ws_bytes = pa.workspace_bytes(cfg.batch, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size,
+                                  cfg.max_blocks_per_seq, pa._dtype_code(tdt), args.partition_size)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache)
+        pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
+                                  partition_size=args.partition_size, workspace=ws, events=events)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for e in events:  # materialise the HIP events outside the timed region
+        e[0].record(stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [e[0].elapsed_time(e[1]) for e in events]
+
+    ms_per_step = wall * 1e3 / args.steps
+    kv_bytes = x.kv_bytes
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    mean_kernel_ms = sum(kernel_ms) / len(kernel_ms)
+    achieved = kv_bytes / (mean_kernel_ms * 1e-3) / 1e9
+
+    # Steps timed after overwriting 1 GiB, so last-level caches hold no KV (reported beside the main figure).
+    cold = []
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_steps):
+            scratch.fill_(1)
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            step(ev)
+            torch.cuda.synchronize()
+            cold.append(ev[0].elapsed_time(ev[1]))
+        del scratch
+
+    traffic = traffic_from_profiles(cfg.name, kv_bytes)
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the workload)",
+        "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
+                       partition_size=args.partition_size, parallelism="single GPU"),
+        "tokens_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel (attention, excludes store and merge)",
+                     "kernel_mean_ms": round(mean_kernel_ms, 5),
+                     "cold_kernel_median_ms": round(sorted(cold)[len(cold) // 2], 5) if cold else None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x, out.cpu().numpy(), args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * pagedattn.h - C ABI of libpagedattn: paged-attention decode for AMD Instinct
+ * MI355X (gfx950, CDNA4).
+ *
+ * What the library computes. The miniVLLM documentation (page "miniVLLM",
+ * section "What is miniVLLM?") describes a KV cache kept in fixed-size pages
+ * and a paged-attention kernel for the decode phase. The hysenlabs review of
+ * MinivLLM (section on the prefilling baseline capped at 128 tokens, closing
+ * paragraph) describes the decode benchmark's baselines: a per-sequence loop
+ * over the paged cache and a batched gather-and-mask version. Both compute, for
+ * every sequence s and query head h, single-query softmax attention over the
+ * sequence's L_s cached tokens:
+ *
+ *     z_t    = scale * <q[s,h,:], K_s[t, h / G, :]>          t = 0 .. L_s - 1
+ *     out[s,h,:] = sum_t exp(z_t - max z) V_s[t, h / G, :] / sum_t exp(z_t - max z)
+ *
+ * with G = num_heads / num_kv_heads query heads per KV head (grouped-query
+ * attention: query head h reads KV head h / G). Token t of sequence s lives at
+ * offset t % block_size of physical block block_tables[s * max_blocks_per_seq
+ * + t / block_size]. The scatter entry point writes each decode step's new
+ * K/V rows into cache slots ("KV cache management" in the same section).
+ *
+ * ----------------------------------------------------------------------------
+ * Physical cache layout (fixed by this library, chosen for gfx950 loads)
+ *
+ *   e = sizeof(element): 4 (fp32) or 2 (fp16, bf16); x = 16 / e.
+ *   k_cache: [num_blocks][num_kv_heads][head_dim / x][block_size][x]
+ *            key element (block b, head g, offset o, dim d) at
+ *            [b][g][d / x][o][d % x]
+ *   v_cache: [num_blocks][num_kv_heads][block_size / 4][head_dim][4]
+ *            value element (b, g, o, d) at [b][g][o / 4][d][o % 4]
+ *
+ * Each (block, kv head) page is one contiguous run of block_size * head_dim * e
+ * bytes in both caches. Inside it, a 16-byte load of the K page holds 16 bytes
+ * of one token's key row, and a load of the V page holds four consecutive
+ * tokens of one or two value dims. Those are the operand shapes of the
+ * matrix-core instructions the decode kernel uses.
+ *
+ * ----------------------------------------------------------------------------
+ * Conventions for every entry point
+ *
+ *  - All data pointers are DEVICE pointers on the current HIP device. Scalars
+ *    and option structs are host values. `stream` is a hipStream_t passed as
+ *    void* (NULL = the default stream).
+ *  - Work is enqueued on `stream` and the call returns without synchronising.
+ *    The library performs no device-to-host reads, so the calls may be
+ *    recorded into a HIP graph once any workspace exists.
+ *  - The caller owns every buffer. The library keeps no pointer after a call
+ *    except its own workspace.
+ *  - Return value: PA_OK (0) on success, otherwise a pa_status code. A thread
+ *    local message is available from pa_last_error(). Argument errors are
+ *    detected on the host before anything is enqueued.
+ *  - Device-side robustness: slots, block ids and context lengths are clamped
+ *    or skipped so that no input value causes an access outside the buffers
+ *    whose sizes the call describes (see each entry point). Out-of-range values
+ *    give unspecified output for the affected sequence, never a fault.
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_DTYPE = 2,       /* unknown dtype, or inputs of different dtypes */
+  PA_ERR_SHAPE = 3,       /* a size is negative/zero where it must be positive, or sizes disagree */
+  PA_ERR_UNSUPPORTED = 4, /* valid request outside what the kernels implement (e.g. head_dim 96) */
+  PA_ERR_WORKSPACE = 5,   /* caller-provided workspace too small or misaligned */
+  PA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_F16 = 1,
+  PA_DTYPE_BF16 = 2
+} pa_dtype;
+
+/*
+ * pa_store_kvcache - write new K/V rows into their cache slots.
+ *
+ * Passage: miniVLLM documentation, "What is miniVLLM?" (paged KV cache
+ * management); hysenlabs MinivLLM review, section on what main.py does (the
+ * engine's block allocation and KV cache management during decode).
+ *
+ * For every token i < num_tokens with slot n = slot_mapping[i] in
+ * [0, num_blocks * block_size): for all kv heads g and dims d,
+ *     K(block n / block_size, g, offset n % block_size, d) = k[i, g, d]
+ *     V(... same ...)                                      = v[i, g, d]
+ * as raw bit copies (no conversion; NaN payloads are preserved).
+ * Tokens whose slot is negative or >= num_blocks * block_size are skipped.
+ * Two tokens with the same slot race (undefined which one lands).
+ *
+ *   k, v            [num_tokens][num_kv_heads][head_dim] of `dtype`; the two
+ *                   inner dims are contiguous; consecutive tokens are
+ *                   k_token_stride / v_token_stride ELEMENTS apart
+ *                   (>= num_kv_heads * head_dim).
+ *   slot_mapping    [num_tokens] int32.
+ *   k_cache, v_cache caches in the layout above, num_blocks blocks, `dtype`.
+ *   head_dim        multiple of x (16-byte chunks), at most 1024.
+ *   block_size      multiple of 4.
+ * num_tokens == 0 is a no-op returning PA_OK.
+ */
+int pa_store_kvcache(const void* k, const void* v, const int32_t* slot_mapping,
+                     void* k_cache, void* v_cache,
+                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int64_t num_blocks,
+                     int64_t k_token_stride, int64_t v_token_stride,
+                     int32_t dtype, void* stream);
+
+/*
+ * pa_paged_attention_decode - single-query attention through block tables.
+ *
+ * Passage: miniVLLM documentation, "What is miniVLLM?" (paged attention for
+ * decode) and "Explore by topic" (online softmax); hysenlabs MinivLLM review,
+ * section on the prefilling baseline capped at 128 tokens (the decode
+ * benchmark's loop and gather-and-mask baselines compute the same result).
+ * The formula is in the file header.
+ *
+ *   q             [num_seqs][num_heads][head_dim] of `dtype`; heads and dims
+ *                 contiguous, consecutive sequences q_seq_stride ELEMENTS apart
+ *                 (>= num_heads * head_dim).
+ *   k_cache, v_cache  num_blocks blocks in the layout above, `dtype`.
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32, contiguous. Entries
+ *                 past ceil(L_s / block_size) are never read. An entry outside
+ *                 [0, num_blocks) is clamped into range (unspecified output).
+ *   context_lens  [num_seqs] int32, L_s. Values are clamped to
+ *                 [0, max_blocks_per_seq * block_size]. L_s == 0 gives zeros.
+ *   scale         softmax scale, applied in fp32 (usually 1/sqrt(head_dim)).
+ *   out           [num_seqs][num_heads][head_dim], contiguous, of out_dtype:
+ *                 PA_DTYPE_F32, or the same dtype as q (rounded to nearest even
+ *                 from the fp32 result).
+ *   Supported: dtype fp32/fp16/bf16; head_dim 64, 128 or 256; block_size a
+ *   power of two in [16, 256]; num_heads a multiple of num_kv_heads (any
+ *   group size G; groups above 16 heads are processed 16 at a time).
+ *   num_seqs at most 16383.
+ *
+ * Long contexts are split across wavefronts and the pieces are merged by a
+ * second kernel (log-sum-exp weighting); see pa_decode_opts. Uses a workspace
+ * owned by the library, allocated or grown on first use for a given size
+ * (that call is not graph-capturable; later calls of the same or smaller size
+ * are). pa_shutdown() frees it. Calls on one device share that workspace, so
+ * calls that may overlap (different streams) must use pa_paged_attention_decode_ex
+ * with workspaces of their own.
+ */
+int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out,
+                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int64_t q_seq_stride,
+                              int32_t dtype, int32_t out_dtype, void* stream);
+
+/*
+ * Options for pa_paged_attention_decode_ex.
+ *
+ * partition_size (tokens):
+ *    0  automatic: the concatenated 16-token tiles of all (sequence, kv head)
+ *       contexts are divided evenly over the wavefronts the device holds at
+ *       once, so long and short sequences finish together; contexts cut by a
+ *       range boundary are merged by the reduce kernel.
+ *   -1  one pass: every (sequence, kv head) context is handled whole by one
+ *       wavefront; no reduce kernel runs.
+ *   >0  fixed ranges of partition_size tokens (a multiple of 16) over the same
+ *       concatenated tile stream.
+ * workspace / workspace_bytes: device memory used instead of the library's own
+ *       (NULL = library-owned). Must be 256-byte aligned and at least
+ *       pa_decode_workspace_bytes(...) bytes. Its contents need no
+ *       initialisation. Calls that share a workspace must not overlap.
+ * event_begin / event_end: optional hipEvent_t handles (as void*) recorded on
+ *       `stream` immediately before and after the attention kernel itself (not
+ *       the reduce kernel), so callers can time that kernel alone.
+ */
+typedef struct pa_decode_opts {
+  int32_t partition_size;
+  int32_t reserved;
+  void* workspace;
+  size_t workspace_bytes;
+  void* event_begin;
+  void* event_end;
+} pa_decode_opts;
+
+int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float scale, void* out,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, int64_t q_seq_stride,
+                                 int32_t dtype, int32_t out_dtype,
+                                 const pa_decode_opts* opts, void* stream);
+
+/*
+ * Launch plan of a decode call: pure host arithmetic, no device access when
+ * num_cus > 0 (num_cus <= 0 queries the current device). Fills any non-NULL
+ * output: the wavefront count of the attention kernel; range_tokens, the
+ * tokens per wavefront range (> 0 fixed, 0 balanced over the data, -1 one
+ * pass); whether the reduce kernel runs; and the workspace bytes the call
+ * needs. Returns the pa_status the decode call would return for these sizes.
+ */
+int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t max_blocks_per_seq, int32_t dtype,
+                   int32_t partition_size, int32_t num_cus,
+                   int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce,
+                   size_t* workspace_bytes);
+
+/* Workspace bytes pa_paged_attention_decode_ex needs for these sizes (0 on bad arguments). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                 int32_t dtype, int32_t partition_size);
+
+/* Message of the last failed call on this thread ("" if none). Never NULL. */
+const char* pa_last_error(void);
+
+/* Library version string, e.g. "libpagedattn 0.1.0 gfx950". */
+const char* pa_version(void);
+
+/* Frees the library-owned workspaces of all devices. Returns PA_OK or PA_ERR_HIP. */
+int pa_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H_ */

@@ -1,0 +1,251 @@
+"""Python binding of libpagedattn (paged-attention decode for MI355X / gfx950).
+
+Argument marshalling only: torch tensors are turned into device pointers,
+sizes, strides and the current HIP stream, and every step runs in the HIP
+kernels of ``libpagedattn.so``. There is no fallback: if the library is not
+built, or a call fails, an exception is raised.
+
+Entry points (same names as the C ABI in ``include/pagedattn.h``):
+
+* ``store_kvcache(k, v, slot_mapping, k_cache, v_cache)``
+* ``paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, ...)``
+
+Cache tensors use the library's physical layout; ``allocate_kv_cache`` creates
+them and ``k_cache_shape`` / ``v_cache_shape`` give the shapes:
+
+* K: ``[num_blocks, num_kv_heads, head_dim // x, block_size, x]`` with
+  ``x = 16 // element_size``
+* V: ``[num_blocks, num_kv_heads, block_size // 4, head_dim, 4]``
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional, Tuple
+
+__all__ = [
+    "PagedAttnError", "store_kvcache", "paged_attention_decode", "allocate_kv_cache",
+    "k_cache_shape", "v_cache_shape", "decode_plan", "workspace_bytes", "version", "shutdown",
+    "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16",
+]
+
+_LIB_PATH = Path(__file__).resolve().with_name("libpagedattn.so")
+_lib = None
+
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_UNSUPPORTED",
+           5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [
+        ("partition_size", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("event_begin", ctypes.c_void_p),
+        ("event_end", ctypes.c_void_p),
+    ]
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpagedattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m paged_attention_decode_amd.build`")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    c_int, c_i64, c_p, c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.pa_store_kvcache.argtypes = [c_p, c_p, c_p, c_p, c_p, c_int, c_int, c_int, c_int, c_i64, c_i64, c_i64,
+                                     c_int, c_p]
+    lib.pa_store_kvcache.restype = c_int
+    dec = [c_p, c_p, c_p, c_p, c_p, c_f, c_p, c_int, c_int, c_int, c_int, c_int, c_int, c_i64, c_i64, c_int, c_int]
+    lib.pa_paged_attention_decode.argtypes = dec + [c_p]
+    lib.pa_paged_attention_decode.restype = c_int
+    lib.pa_paged_attention_decode_ex.argtypes = dec + [ctypes.POINTER(DecodeOpts), c_p]
+    lib.pa_paged_attention_decode_ex.restype = c_int
+    lib.pa_decode_plan.argtypes = [c_int] * 9 + [ctypes.POINTER(c_i64), ctypes.POINTER(c_int),
+                                                 ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_decode_plan.restype = c_int
+    lib.pa_decode_workspace_bytes.argtypes = [c_int] * 8
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    lib.pa_shutdown.argtypes = []
+    lib.pa_shutdown.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PagedAttnError(rc, load_library().pa_last_error().decode())
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    codes = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+    if dt not in codes:
+        raise TypeError(f"unsupported dtype {dt}")
+    return codes[dt]
+
+
+def _elem(dt) -> int:
+    import torch
+    return torch.empty((), dtype=dt).element_size()
+
+
+def k_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype) -> Tuple[int, ...]:
+    x = 16 // _elem(dtype)
+    return (num_blocks, num_kv_heads, head_dim // x, block_size, x)
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype=None) -> Tuple[int, ...]:
+    return (num_blocks, num_kv_heads, block_size // 4, head_dim, 4)
+
+
+def allocate_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype, device="cuda"):
+    """Uninitialised (k_cache, v_cache) in the library's physical layout."""
+    import torch
+    k = torch.empty(k_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype), dtype=dtype, device=device)
+    v = torch.empty(v_cache_shape(num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+    return k, v
+
+
+def _stream_of(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _cache_geometry(k_cache, v_cache):
+    if k_cache.dim() != 5 or v_cache.dim() != 5:
+        raise ValueError("k_cache and v_cache must be 5-D tensors in the library layout")
+    nb, hkv, chunks, bs, x = k_cache.shape
+    if x != 16 // k_cache.element_size():
+        raise ValueError(f"k_cache innermost dim {x} must be {16 // k_cache.element_size()}")
+    d = chunks * x
+    if tuple(v_cache.shape) != (nb, hkv, bs // 4, d, 4):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache dtypes differ")
+    return nb, hkv, d, bs
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def store_kvcache(k, v, slot_mapping, k_cache, v_cache) -> None:
+    """Write k[i], v[i] ([N, Hkv, D]) into slot slot_mapping[i] of the caches (slots < 0 skipped)."""
+    import torch
+    lib = load_library()
+    _require_cuda(k, v, slot_mapping, k_cache, v_cache)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    if k.dim() != 3 or v.dim() != 3 or tuple(k.shape[1:]) != (hkv, d) or tuple(v.shape[1:]) != (hkv, d):
+        raise ValueError(f"k, v must be [N, {hkv}, {d}], got {tuple(k.shape)}, {tuple(v.shape)}")
+    if k.shape[0] != v.shape[0] or slot_mapping.shape != (k.shape[0],):
+        raise ValueError("k, v and slot_mapping disagree on the token count")
+    if slot_mapping.dtype != torch.int32 or not slot_mapping.is_contiguous():
+        raise TypeError("slot_mapping must be a contiguous int32 tensor")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype:
+        raise TypeError("k, v and the caches must share one dtype")
+    for t in (k, v):
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError("k and v need contiguous [Hkv, D] rows")
+    _check(lib.pa_store_kvcache(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+                                v_cache.data_ptr(), k.shape[0], hkv, d, bs, nb, k.stride(0), v.stride(0),
+                                _dtype_code(k.dtype), _stream_of(k_cache)))
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
+                           out_dtype=None, partition_size: int = 0, workspace=None, events=None):
+    """Decode attention; returns ``out`` ([B, Hq, D], fp32 or q's dtype).
+
+    partition_size: 0 balanced split (default), -1 one pass per sequence,
+    >0 fixed ranges of that many tokens. workspace: optional uint8 CUDA tensor
+    (see ``workspace_bytes``). events: optional (begin, end) torch.cuda.Event
+    pair recorded around the attention kernel itself.
+    """
+    import torch
+    lib = load_library()
+    _require_cuda(q, k_cache, v_cache, block_tables, context_lens)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != d or q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError(f"q must be [B, Hq, {d}] with contiguous head rows")
+    bsz, hq = q.shape[0], q.shape[1]
+    if q.dtype != k_cache.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != bsz or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous [B, max_blocks] tensor")
+    if context_lens.shape != (bsz,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] tensor")
+    if out is None:
+        odt = out_dtype if out_dtype is not None else q.dtype
+        out = torch.empty((bsz, hq, d), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (bsz, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor")
+    opts = DecodeOpts()
+    opts.partition_size = int(partition_size)
+    if workspace is not None:
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    if events is not None:
+        for ev in events:
+            if not ev.cuda_event:
+                ev.record()  # a torch event gets its HIP handle on first record
+        opts.event_begin = events[0].cuda_event
+        opts.event_end = events[1].cuda_event
+    _check(lib.pa_paged_attention_decode_ex(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+        float(scale), out.data_ptr(), bsz, hq, hkv, d, bs, block_tables.shape[1], nb, q.stride(0),
+        _dtype_code(q.dtype), _dtype_code(out.dtype), ctypes.byref(opts), _stream_of(q)))
+    return out
+
+
+def decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype_code,
+                partition_size=0, num_cus=256) -> dict:
+    """Host-only launch plan (no device access when num_cus > 0)."""
+    lib = load_library()
+    waves = ctypes.c_int64()
+    rng = ctypes.c_int32()
+    red = ctypes.c_int32()
+    ws = ctypes.c_size_t()
+    _check(lib.pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              dtype_code, partition_size, num_cus, ctypes.byref(waves), ctypes.byref(rng),
+                              ctypes.byref(red), ctypes.byref(ws)))
+    return {"num_waves": waves.value, "range_tokens": rng.value, "uses_reduce": bool(red.value),
+            "workspace_bytes": ws.value}
+
+
+def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype_code,
+                    partition_size=0) -> int:
+    return int(load_library().pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                                       max_blocks_per_seq, dtype_code, partition_size))
+
+
+def version() -> str:
+    return load_library().pa_version().decode()
+
+
+def shutdown() -> None:
+    _check(load_library().pa_shutdown())

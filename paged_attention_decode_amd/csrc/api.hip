@@ -1,0 +1,371 @@
+// Host side of libpagedattn: argument checks, launch planning, workspace and
+// the extern "C" entry points declared in include/pagedattn.h.
+
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <climits>
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace {
+
+using namespace pa;
+
+thread_local std::string t_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_error = buf;
+  return code;
+}
+
+int ok() {
+  t_error.clear();
+  return PA_OK;
+}
+
+// Attention-kernel workgroups per compute unit that one call plans for.
+// Ranges are sized for this many resident wavefronts (4 per workgroup).
+constexpr int kGroupsPerCU = 2;
+
+struct DeviceState {
+  bool init = false;
+  int num_cus = 0;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+
+std::mutex g_mutex;
+std::vector<DeviceState> g_devices;
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Plan {
+  int64_t num_waves = 0;
+  int grid = 0;
+  int range_tiles = 0;  // -1 one pass, 0 balanced, >0 fixed
+  bool reduce = false;
+  size_t lds = 0;
+  int n_hg = 0, gh_max = 0, segs_per_seq = 0;
+  size_t off_lse = 0, off_meta = 0, ws_bytes = 0;
+};
+
+bool valid_dtype(int dt) { return dt == PA_DTYPE_F32 || dt == PA_DTYPE_F16 || dt == PA_DTYPE_BF16; }
+
+int check_decode_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks, int32_t dtype, int32_t partition_size) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_DTYPE, "dtype %d is not one of PA_DTYPE_F32/F16/BF16", dtype);
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "num_seqs %d < 0", num_seqs);
+  if (num_seqs > kMaxSeqs) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds %d", num_seqs, kMaxSeqs);
+  if (num_heads <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_SHAPE, "num_heads %d and num_kv_heads %d must be positive", num_heads, num_kv_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+  if (head_dim <= 0) return fail(PA_ERR_SHAPE, "head_dim %d must be positive", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128, 256)", head_dim);
+  if (block_size <= 0) return fail(PA_ERR_SHAPE, "block_size %d must be positive", block_size);
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 256)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (power of two in [16, 256])", block_size);
+  if (max_blocks <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks);
+  if ((int64_t)max_blocks * block_size > INT32_MAX / 2)
+    return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size too large");
+  if (partition_size < -1 || (partition_size > 0 && partition_size % kTile != 0))
+    return fail(PA_ERR_SHAPE, "partition_size %d must be -1, 0 or a positive multiple of 16", partition_size);
+  return PA_OK;
+}
+
+int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t max_blocks, int32_t partition_size, int num_cus, Plan* p) {
+  const int group = num_heads / num_kv_heads;
+  p->n_hg = (group + kHeadsPerTile - 1) / kHeadsPerTile;
+  p->gh_max = group < kHeadsPerTile ? group : kHeadsPerTile;
+  p->segs_per_seq = num_kv_heads * p->n_hg;
+  const int64_t segs = (int64_t)num_seqs * p->segs_per_seq;
+  const int64_t max_tiles = ((int64_t)max_blocks * block_size + kTile - 1) / kTile;
+  const int64_t upper_tiles = segs * (max_tiles > 0 ? max_tiles : 1);
+  const int64_t resident = (int64_t)num_cus * kGroupsPerCU * kWavesPerGroup;
+  int64_t waves;
+  if (partition_size < 0) {
+    p->range_tiles = -1;
+    waves = segs < resident ? segs : resident;
+    p->lds = 0;
+    p->reduce = false;
+  } else {
+    if (upper_tiles + max_tiles >= INT32_MAX / 2)
+      return fail(PA_ERR_UNSUPPORTED, "batch too large: %lld tiles", (long long)upper_tiles);
+    p->lds = (size_t)(num_seqs + 1) * sizeof(int32_t);
+    p->reduce = true;
+    if (partition_size == 0) {
+      p->range_tiles = 0;
+      const int64_t useful = (upper_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave;
+      waves = useful < resident ? useful : resident;
+    } else {
+      p->range_tiles = partition_size / kTile;
+      waves = (upper_tiles + p->range_tiles - 1) / p->range_tiles;
+    }
+  }
+  if (waves < 1) waves = 1;
+  p->grid = (int)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
+  p->num_waves = (int64_t)p->grid * kWavesPerGroup;
+  if (p->reduce) {
+    const size_t rows = (size_t)p->num_waves * 2 * p->gh_max;
+    p->off_lse = align256(rows * head_dim * sizeof(float));
+    p->off_meta = p->off_lse + align256(rows * sizeof(float));
+    p->ws_bytes = p->off_meta + align256((size_t)segs * sizeof(int4));
+  } else {
+    p->off_lse = p->off_meta = p->ws_bytes = 0;
+  }
+  return PA_OK;
+}
+
+int device_state(DeviceState** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if ((int)g_devices.size() <= dev) g_devices.resize(dev + 1);
+  DeviceState& st = g_devices[dev];
+  if (!st.init) {
+    int cus = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0) return fail(PA_ERR_HIP, "cannot query compute units: %s", hipGetErrorString(e));
+    st.num_cus = cus;
+    st.init = true;
+  }
+  *out = &st;
+  return PA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_store_kvcache(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int64_t num_blocks, int64_t k_token_stride, int64_t v_token_stride, int32_t dtype,
+                     void* stream) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_DTYPE, "dtype %d is not one of PA_DTYPE_F32/F16/BF16", dtype);
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+  const int e = elem_bytes(dtype);
+  const int x = 16 / e;
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE, "num_kv_heads %d, head_dim %d, block_size %d, num_blocks %lld must be positive",
+                num_kv_heads, head_dim, block_size, (long long)num_blocks);
+  if (head_dim % x != 0 || head_dim > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d must be a multiple of %d and at most 1024", head_dim, x);
+  if (block_size % 4 != 0) return fail(PA_ERR_UNSUPPORTED, "block_size %d must be a multiple of 4", block_size);
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_NULL, "a required pointer is NULL");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (k_token_stride < row || v_token_stride < row)
+    return fail(PA_ERR_SHAPE, "token strides (%lld, %lld) smaller than num_kv_heads*head_dim %lld",
+                (long long)k_token_stride, (long long)v_token_stride, (long long)row);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (k_token_stride * e) % 16 != 0 || (v_token_stride * e) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "k, v and the caches must be 16-byte aligned with 16-byte token strides");
+  if ((int64_t)num_tokens * num_kv_heads * (head_dim / x) > (int64_t)INT32_MAX * 256)
+    return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+  StoreArgs a;
+  a.k = k;
+  a.v = v;
+  a.slot_mapping = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.num_slots = num_blocks * block_size;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  hipError_t err = launch_store(a, dtype, reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "store_kvcache launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
+int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t max_blocks_per_seq, int32_t dtype, int32_t partition_size, int32_t num_cus,
+                   int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce, size_t* workspace_bytes) {
+  int rc = check_decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
+                              partition_size);
+  if (rc != PA_OK) return rc;
+  if (num_cus <= 0) {
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc != PA_OK) return rc;
+    num_cus = st->num_cus;
+  }
+  Plan p;
+  rc = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, partition_size,
+                 num_cus, &p);
+  if (rc != PA_OK) return rc;
+  if (num_waves) *num_waves = p.num_waves;
+  if (range_tokens) *range_tokens = p.range_tiles > 0 ? p.range_tiles * kTile : p.range_tiles;
+  if (uses_reduce) *uses_reduce = p.reduce ? 1 : 0;
+  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq, int32_t dtype,
+                                 int32_t partition_size) {
+  size_t bytes = 0;
+  if (pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
+                     partition_size, 0, nullptr, nullptr, nullptr, &bytes) != PA_OK)
+    return 0;
+  return bytes;
+}
+
+int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int64_t q_seq_stride, int32_t dtype, int32_t out_dtype,
+                                 const pa_decode_opts* opts, void* stream) {
+  const int32_t psize = opts ? opts->partition_size : 0;
+  int rc = check_decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
+                              psize);
+  if (rc != PA_OK) return rc;
+  if (!valid_dtype(out_dtype) || (out_dtype != PA_DTYPE_F32 && out_dtype != dtype))
+    return fail(PA_ERR_DTYPE, "out_dtype %d must be PA_DTYPE_F32 or the input dtype %d", out_dtype, dtype);
+  if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %lld must be positive", (long long)num_blocks);
+  if (q_seq_stride < (int64_t)num_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "q_seq_stride %lld smaller than num_heads*head_dim", (long long)q_seq_stride);
+  if (num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  const int e = elem_bytes(dtype);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (q_seq_stride * e) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "q, the caches and out must be 16-byte aligned (q rows too)");
+
+  DeviceState* st = nullptr;
+  rc = device_state(&st);
+  if (rc != PA_OK) return rc;
+  Plan p;
+  rc = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, psize, st->num_cus, &p);
+  if (rc != PA_OK) return rc;
+
+  char* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    if (opts && opts->workspace) {
+      if (opts->workspace_bytes < p.ws_bytes)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", opts->workspace_bytes, p.ws_bytes);
+      if ((reinterpret_cast<uintptr_t>(opts->workspace) & 255u) != 0)
+        return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+      ws = reinterpret_cast<char*>(opts->workspace);
+    } else {
+      std::lock_guard<std::mutex> lock(g_mutex);
+      if (st->ws_bytes < p.ws_bytes) {
+        if (st->ws) {
+          (void)hipFree(st->ws);
+          st->ws = nullptr;
+          st->ws_bytes = 0;
+        }
+        void* mem = nullptr;
+        hipError_t err = hipMalloc(&mem, p.ws_bytes);
+        if (err != hipSuccess)
+          return fail(PA_ERR_HIP, "workspace allocation of %zu bytes failed: %s", p.ws_bytes, hipGetErrorString(err));
+        st->ws = mem;
+        st->ws_bytes = p.ws_bytes;
+      }
+      ws = reinterpret_cast<char*>(st->ws);
+    }
+  }
+
+  DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_lse = ws ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
+  a.ws_meta = ws ? reinterpret_cast<int4*>(ws + p.off_meta) : nullptr;
+  a.q_seq_stride = q_seq_stride;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.n_hg = p.n_hg;
+  a.gh_max = p.gh_max;
+  a.segs_per_seq = p.segs_per_seq;
+  a.block_size = block_size;
+  a.bs_log2 = ilog2(block_size);
+  a.max_blocks = max_blocks_per_seq;
+  a.out_f32 = out_dtype == PA_DTYPE_F32 ? 1 : 0;
+  a.num_waves = (int32_t)p.num_waves;
+  a.range_tiles = p.range_tiles;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (opts && opts->event_begin) {
+    hipError_t err = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->event_begin), s);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord(begin) failed: %s", hipGetErrorString(err));
+  }
+  hipError_t err = launch_decode(a, dtype, head_dim, p.grid, p.lds, s);
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
+  if (opts && opts->event_end) {
+    err = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->event_end), s);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord(end) failed: %s", hipGetErrorString(err));
+  }
+  if (p.reduce) {
+    err = launch_reduce(a, dtype, head_dim, s);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "reduce launch failed: %s", hipGetErrorString(err));
+  }
+  return ok();
+}
+
+int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t max_blocks_per_seq, int64_t num_blocks, int64_t q_seq_stride, int32_t dtype,
+                              int32_t out_dtype, void* stream) {
+  return pa_paged_attention_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                                      num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                      q_seq_stride, dtype, out_dtype, nullptr, stream);
+}
+
+const char* pa_last_error(void) { return t_error.c_str(); }
+
+const char* pa_version(void) { return "libpagedattn 0.1.0 gfx950"; }
+
+int pa_shutdown(void) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  int rc = PA_OK;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+  for (size_t d = 0; d < g_devices.size(); ++d) {
+    DeviceState& st = g_devices[d];
+    if (!st.ws) continue;
+    if (hipSetDevice((int)d) != hipSuccess || hipFree(st.ws) != hipSuccess) rc = PA_ERR_HIP;
+    st.ws = nullptr;
+    st.ws_bytes = 0;
+  }
+  if (cur >= 0) (void)hipSetDevice(cur);
+  if (rc != PA_OK) return fail(rc, "hipFree of a workspace failed");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,555 @@
+// Paged-attention decode kernels for gfx950 (CDNA4).
+//
+// Operation: single-query softmax attention of every (sequence, query head)
+// over the sequence's cached tokens, read through its block table
+// (miniVLLM documentation, "What is miniVLLM?": paged attention for decode
+// over a paged KV cache; online softmax as in "Explore by topic" there and in
+// the tiny-vllm note, "Chi tiết"). The formula is in include/pagedattn.h.
+//
+// Work decomposition. A segment is one (sequence, kv head, group of up to 16
+// query heads); it has ceil(L/16) tiles of 16 tokens. The tiles of all
+// segments are concatenated in (sequence, kv head, head group) order and cut
+// into equal ranges, one per wavefront, so every wavefront streams the same
+// number of KV bytes however skewed the lengths are. A segment that lies
+// inside one range is finished by its wavefront (output written directly);
+// a segment cut by range boundaries leaves one normalised partial output and
+// its log2-sum-exp2 per piece, merged afterwards by reduce_kernel.
+//
+// Per 16-token tile, one wavefront computes
+//   S[t][h]   = K[t][:] . Q[h][:]          (matrix core: rows = tokens, cols = heads)
+//   online softmax on S (running max m, running sum l, per head = per lane column)
+//   O^T[d][h] += V^T[d][t] . P^T[t][h]     (matrix core: rows = dims, cols = heads)
+// The result layout of the first product (lane = 16*row_group + head, four
+// token rows per lane) is exactly the operand layout the second product needs
+// for P^T, so P never leaves registers. The cache layout (pagedattn.h) makes
+// every 16-byte global load land directly in the operand registers of these
+// instructions: no LDS staging, no transposes. K/V of the next tile are in
+// flight while the current tile is computed.
+//
+// Numerics: products and accumulation in fp32. For fp16/bf16 inputs the
+// softmax weights P enter the second product as a sum of two 16-bit numbers
+// (rounded value + rounded remainder), so the weights keep ~16 significant
+// bits instead of 8 (bf16) or 11 (fp16).
+
+#include "pa_internal.h"
+
+#include <math.h>
+
+namespace pa {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef _Float16 h4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
+typedef _Float16 h8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef __bf16 b8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef unsigned int u2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+
+template <int DT, int D>
+struct Cfg {
+  static constexpr int kE = (DT == kF32) ? 4 : 2;  // bytes per element
+  static constexpr int kX = 16 / kE;               // elements per 16-byte chunk
+  static constexpr int kChunks = D / kX;           // 16-byte chunks per key row
+  static constexpr int kLoads = kChunks / 4;       // 16-byte loads per lane per tile (K, and V)
+  static constexpr int kAcc = D / 16;              // 16x16 accumulator tiles of O^T
+};
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  // Round to nearest even; inputs here are finite.
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int clamp_len(int L, int max_len) {
+  return L < 0 ? 0 : (L > max_len ? max_len : L);
+}
+
+// Write 8 consecutive output values (d0 .. d0+7) of one head row.
+template <int DT>
+__device__ __forceinline__ void store8(void* out, int64_t idx, const float (&v)[8], bool out_f32) {
+  if (out_f32) {
+    f4* p = reinterpret_cast<f4*>(reinterpret_cast<float*>(out) + idx);
+    p[0] = f4{v[0], v[1], v[2], v[3]};
+    p[1] = f4{v[4], v[5], v[6], v[7]};
+  } else if constexpr (DT == kBF16) {
+    u4 w;
+    w.x = bf16_bits_rne(v[0]) | (bf16_bits_rne(v[1]) << 16);
+    w.y = bf16_bits_rne(v[2]) | (bf16_bits_rne(v[3]) << 16);
+    w.z = bf16_bits_rne(v[4]) | (bf16_bits_rne(v[5]) << 16);
+    w.w = bf16_bits_rne(v[6]) | (bf16_bits_rne(v[7]) << 16);
+    *reinterpret_cast<u4*>(reinterpret_cast<uint16_t*>(out) + idx) = w;
+  } else if constexpr (DT == kF16) {
+    h8 w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = (_Float16)v[j];
+    *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(out) + idx) = w;
+  }
+}
+
+template <int DT, int D>
+struct Piece {
+  using C = Cfg<DT, D>;
+
+  // Runs tiles [lt0, lt1) of segment (s, r). complete: the piece is the whole
+  // segment, so the normalised result goes straight to `out`; otherwise to
+  // workspace slot `slot` of this wavefront.
+  static __device__ __forceinline__ void run(const DecodeArgs& a, int s, int r, int L, int lt0, int lt1,
+                                             bool complete, int wave, int slot, int lane) {
+    const int kq = lane >> 4;  // operand k-group, and result row group
+    const int ln = lane & 15;  // operand row, and result column (= head in group)
+    const int g = r / a.n_hg;
+    const int hg = r - g * a.n_hg;
+    const int h0 = g * a.group + hg * kHeadsPerTile;
+    const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
+    const int bs = a.block_size;
+
+    // Query operand: Q[h0 + ln][16-byte chunk 4j + kq]; zero for padding columns.
+    u4 qv[C::kLoads];
+    {
+      const char* qrow = reinterpret_cast<const char*>(a.q) +
+                         ((int64_t)s * a.q_seq_stride + (int64_t)(h0 + ln) * D) * C::kE;
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j)
+        qv[j] = (ln < gh) ? *reinterpret_cast<const u4*>(qrow + (4 * j + kq) * 16) : u4{0u, 0u, 0u, 0u};
+    }
+
+    f4 acc[C::kAcc];
+#pragma unroll
+    for (int u = 0; u < C::kAcc; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+    float l = 0.f;
+
+    if (L > 0) {
+      const int64_t page_bytes = (int64_t)bs * D * C::kE;
+      const int64_t blk_stride = (int64_t)a.num_kv_heads * page_bytes;
+      const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * page_bytes;
+      const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * page_bytes;
+      const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+      const int64_t nb_max = a.num_blocks - 1;
+      // Lane offsets inside a page. K: chunk (4j + kq) of token (off0 + ln).
+      // V (16-bit): dims 32w + 2ln, +1 of tokens off0 + 4kq .. +3.
+      // V (fp32):   dim 16u + ln of tokens off0 + 4kq .. +3.
+      const uint32_t k_lane = (uint32_t)((kq * bs + ln) * 16);
+      const uint32_t v_lane = (DT == kF32) ? (uint32_t)((kq * D + ln) * 16) : (uint32_t)((kq * D + 2 * ln) * 8);
+
+      // Block-table entries, 64 pages at a time, one per lane.
+      int bt_first = INT32_MIN / 2;
+      int bt_val = 0;
+
+      auto load_tile = [&](int i, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+        const int t0 = i * kTile;
+        const int page = t0 >> a.bs_log2;
+        const int off0 = t0 & (bs - 1);
+        if (page - bt_first >= 64 || page < bt_first) {
+          bt_first = page;
+          const int idx = page + lane;
+          bt_val = idx < a.max_blocks ? bt[idx] : 0;
+        }
+        int64_t blk = __builtin_amdgcn_readlane(bt_val, page - bt_first);
+        blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
+        const char* kp = kbase + blk * blk_stride + off0 * 16;
+        const char* vp = vbase + blk * blk_stride + (int64_t)off0 * D * C::kE;
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j)
+          kb[j] = *reinterpret_cast<const u4*>(kp + k_lane + j * 64 * bs);
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j)
+          vb[j] = *reinterpret_cast<const u4*>(vp + v_lane + j * 256);
+      };
+
+      auto compute_tile = [&](int i, const u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+        // S[token 4kq + r][head ln] for r = 0..3
+        f4 sv = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j) {
+          if constexpr (DT == kF32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sv = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kb[j][e]), __uint_as_float(qv[j][e]), sv, 0, 0, 0);
+          } else if constexpr (DT == kBF16) {
+            sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, kb[j]), __builtin_bit_cast(b8, qv[j]), sv, 0, 0, 0);
+          } else {
+            sv = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kb[j]), __builtin_bit_cast(h8, qv[j]), sv, 0, 0, 0);
+          }
+        }
+        const int t0 = i * kTile;
+        const bool partial = (t0 + kTile > L);
+        float z[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          z[rr] = sv[rr] * a.scale_log2;
+          if (partial && (t0 + 4 * kq + rr >= L)) z[rr] = -INFINITY;
+        }
+        float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m, mt);
+        const float alpha = exp2_fast(m - m_new);
+        float p[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) p[rr] = exp2_fast(z[rr] - m_new);
+        l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m = m_new;
+#pragma unroll
+        for (int u = 0; u < C::kAcc; ++u) acc[u] *= alpha;
+
+        if (partial) {
+          // Zero the values of tokens past the end: a NaN there must not reach the sums.
+          const bool v0 = t0 + 4 * kq + 0 < L, v1 = t0 + 4 * kq + 1 < L;
+          const bool v2 = t0 + 4 * kq + 2 < L, v3 = t0 + 4 * kq + 3 < L;
+          if constexpr (DT == kF32) {
+            const u4 msk = u4{v0 ? ~0u : 0u, v1 ? ~0u : 0u, v2 ? ~0u : 0u, v3 ? ~0u : 0u};
+#pragma unroll
+            for (int j = 0; j < C::kLoads; ++j) vb[j] &= msk;
+          } else {
+            const uint32_t m01 = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
+            const uint32_t m23 = (v2 ? 0x0000FFFFu : 0u) | (v3 ? 0xFFFF0000u : 0u);
+            const u4 msk = u4{m01, m23, m01, m23};
+#pragma unroll
+            for (int j = 0; j < C::kLoads; ++j) vb[j] &= msk;
+          }
+        }
+
+        if constexpr (DT == kF32) {
+#pragma unroll
+          for (int u = 0; u < C::kLoads; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb[u][e]), p[e], acc[u], 0, 0, 0);
+        } else if constexpr (DT == kBF16) {
+          s4 ph, pl;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t hb = bf16_bits_rne(p[rr]);
+            const float rem = p[rr] - __uint_as_float(hb << 16);
+            ph[rr] = (short)hb;
+            pl[rr] = (short)bf16_bits_rne(rem);
+          }
+#pragma unroll
+          for (int w = 0; w < C::kLoads; ++w) {
+            const s4 a0 = __builtin_bit_cast(s4, u2{vb[w].x, vb[w].y});
+            const s4 a1 = __builtin_bit_cast(s4, u2{vb[w].z, vb[w].w});
+            acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, ph, acc[2 * w], 0, 0, 0);
+            acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, pl, acc[2 * w], 0, 0, 0);
+            acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, ph, acc[2 * w + 1], 0, 0, 0);
+            acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, pl, acc[2 * w + 1], 0, 0, 0);
+          }
+        } else {
+          h4 ph, pl;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const _Float16 hi = (_Float16)p[rr];
+            ph[rr] = hi;
+            pl[rr] = (_Float16)(p[rr] - (float)hi);
+          }
+#pragma unroll
+          for (int w = 0; w < C::kLoads; ++w) {
+            const h4 a0 = __builtin_bit_cast(h4, u2{vb[w].x, vb[w].y});
+            const h4 a1 = __builtin_bit_cast(h4, u2{vb[w].z, vb[w].w});
+            acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, ph, acc[2 * w], 0, 0, 0);
+            acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, pl, acc[2 * w], 0, 0, 0);
+            acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, ph, acc[2 * w + 1], 0, 0, 0);
+            acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, pl, acc[2 * w + 1], 0, 0, 0);
+          }
+        }
+      };
+
+      // Two register sets: the loads of tile i+1 are in flight while tile i is computed.
+      u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads];
+      int i = lt0;
+      load_tile(i, kA, vA);
+      while (true) {
+        const bool has_b = i + 1 < lt1;
+        if (has_b) load_tile(i + 1, kB, vB);
+        compute_tile(i, kA, vA);
+        if (!has_b) break;
+        const bool has_a = i + 2 < lt1;
+        if (has_a) load_tile(i + 2, kA, vA);
+        compute_tile(i + 1, kB, vB);
+        if (!has_a) break;
+        i += 2;
+      }
+    }
+
+    // Sum of the four row groups' partial sums of each head column.
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = (L > 0) ? 1.0f / lt : 0.0f;
+    if (ln >= gh) return;
+
+    float* dst_f32 = nullptr;
+    void* dst = a.out;
+    int64_t base;
+    bool as_f32 = a.out_f32 != 0;
+    if (complete) {
+      base = ((int64_t)s * a.num_heads + h0 + ln) * D;
+    } else {
+      const int64_t row = ((int64_t)wave * 2 + slot) * a.gh_max + ln;
+      dst_f32 = a.ws_o;
+      dst = dst_f32;
+      base = row * D;
+      as_f32 = true;
+      if (kq == 0) a.ws_lse[row] = m + __log2f(lt);
+    }
+    if constexpr (DT == kF32) {
+      // O^T tile u holds dims 16u + 4kq + r.
+#pragma unroll
+      for (int u = 0; u < C::kAcc; ++u) {
+        f4 v = acc[u] * inv;
+        *reinterpret_cast<f4*>(reinterpret_cast<float*>(dst) + base + 16 * u + 4 * kq) = v;
+      }
+    } else {
+      // O^T tiles 2w (even dims) and 2w+1 (odd dims) hold dims 32w + 8kq + 2r + parity.
+#pragma unroll
+      for (int w = 0; w < C::kLoads; ++w) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = acc[2 * w + (j & 1)][j >> 1] * inv;
+        store8<DT>(dst, base + 32 * w + 8 * kq, v, as_f32);
+      }
+    }
+  }
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
+  extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]: first global tile of each sequence
+  __shared__ int32_t s_wsum[kWavesPerGroup];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int max_len = a.max_blocks << a.bs_log2;
+  const int H = a.segs_per_seq;
+
+  if (a.range_tiles < 0) {
+    // One pass: each wavefront takes whole segments.
+    const int nseg = a.num_seqs * H;
+    for (int seg = wave; seg < nseg; seg += a.num_waves) {
+      const int s = seg / H;
+      const int r = seg - s * H;
+      const int L = clamp_len(a.context_lens[s], max_len);
+      const int tiles = max(1, (L + kTile - 1) / kTile);
+      Piece<DT, D>::run(a, s, r, L, 0, tiles, true, wave, 0, lane);
+    }
+    return;
+  }
+
+  // Prefix sums of tiles per sequence (every segment has at least one tile,
+  // so an empty sequence still gets a wavefront that writes its zeros).
+  int carry = 0;
+  for (int base = 0; base < a.num_seqs; base += kDecodeThreads) {
+    const int i = base + tid;
+    int v = 0;
+    if (i < a.num_seqs) {
+      const int L = clamp_len(a.context_lens[i], max_len);
+      v = max(1, (L + kTile - 1) / kTile) * H;
+    }
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[tid >> 6] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) {
+      const int sw = s_wsum[w];
+      before += (w < (tid >> 6)) ? sw : 0;
+      total += sw;
+    }
+    if (i < a.num_seqs) s_prefix[i + 1] = carry + before + x;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) s_prefix[0] = 0;
+  __syncthreads();
+
+  const int total = s_prefix[a.num_seqs];
+  int R;
+  if (a.range_tiles > 0) {
+    R = a.range_tiles;
+  } else {
+    const int n_eff = min(a.num_waves, max(1, (total + kMinTilesPerWave - 1) / kMinTilesPerWave));
+    R = (total + n_eff - 1) / n_eff;
+  }
+  int t = wave * R;
+  if (t >= total) return;
+  const int t_end = min(total, t + R);
+
+  // Sequence holding tile t: largest s with s_prefix[s] <= t.
+  int lo = 0, hi = a.num_seqs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_prefix[mid] <= t) lo = mid; else hi = mid;
+  }
+  int s = lo;
+  int L = clamp_len(a.context_lens[s], max_len);
+  int tiles = max(1, (L + kTile - 1) / kTile);
+  const int local = t - s_prefix[s];
+  int r = local / tiles;
+  int lt = local - r * tiles;
+  bool first = true;
+  while (true) {
+    const int n = min(tiles - lt, t_end - t);
+    const bool complete = (lt == 0) && (n == tiles);
+    const int slot = first ? 0 : 1;
+    if (lt == 0 && lane == 0) {
+      // This wavefront holds the segment's first piece: record where all pieces are.
+      a.ws_meta[(int64_t)s * H + r] = make_int4(wave, slot, (t + tiles - 1) / R, 0);
+    }
+    Piece<DT, D>::run(a, s, r, L, lt, lt + n, complete, wave, slot, lane);
+    t += n;
+    if (t >= t_end) break;
+    first = false;
+    lt = 0;
+    if (++r == H) {
+      r = 0;
+      ++s;
+      L = clamp_len(a.context_lens[s], max_len);
+      tiles = max(1, (L + kTile - 1) / kTile);
+    }
+  }
+}
+
+// Merge of the pieces of every cut segment: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),
+// M = max_p lse_p, pieces taken in wavefront order (deterministic).
+template <int DT, int D>
+__global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
+  constexpr int kPer = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int seg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (seg >= a.num_seqs * a.segs_per_seq) return;
+  const int4 meta = a.ws_meta[seg];
+  const int wa = meta.x, slot_a = meta.y, wb = meta.z;
+  if (wb <= wa) return;  // finished inside one wavefront
+  const int s = seg / a.segs_per_seq;
+  const int r = seg - s * a.segs_per_seq;
+  const int g = r / a.n_hg;
+  const int hg = r - g * a.n_hg;
+  const int h0 = g * a.group + hg * kHeadsPerTile;
+  const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
+  for (int n = 0; n < gh; ++n) {
+    float M = -INFINITY;
+    for (int w = wa; w <= wb; ++w) {
+      const int sl = (w == wa) ? slot_a : 0;
+      M = fmaxf(M, a.ws_lse[((int64_t)w * 2 + sl) * a.gh_max + n]);
+    }
+    float accv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) accv[k] = 0.f;
+    float wsum = 0.f;
+    for (int w = wa; w <= wb; ++w) {
+      const int sl = (w == wa) ? slot_a : 0;
+      const int64_t row = ((int64_t)w * 2 + sl) * a.gh_max + n;
+      const float x = a.ws_lse[row];
+      const float wt = (x == -INFINITY) ? 0.f : exp2_fast(x - M);
+      wsum += wt;
+      const float* o = a.ws_o + row * D + lane * kPer;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) accv[k] += wt * o[k];
+    }
+    const float inv = 1.0f / wsum;
+    const int64_t obase = ((int64_t)s * a.num_heads + h0 + n) * D + lane * kPer;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const float v = accv[k] * inv;
+      if (a.out_f32) {
+        reinterpret_cast<float*>(a.out)[obase + k] = v;
+      } else if constexpr (DT == kBF16) {
+        reinterpret_cast<uint16_t*>(a.out)[obase + k] = (uint16_t)bf16_bits_rne(v);
+      } else if constexpr (DT == kF16) {
+        reinterpret_cast<_Float16*>(a.out)[obase + k] = (_Float16)v;
+      }
+    }
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_decode_t(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<DT, D>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
+  const int nseg = a.num_seqs * a.segs_per_seq;
+  hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((nseg + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t occupancy_t(size_t lds, int* groups) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups, decode_kernel<DT, D>, kDecodeThreads, lds);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid, size_t lds, hipStream_t st) {
+  switch (dtype) {
+    case kF32:
+      if (head_dim == 64) return launch_decode_t<kF32, 64>(a, grid, lds, st);
+      if (head_dim == 128) return launch_decode_t<kF32, 128>(a, grid, lds, st);
+      if (head_dim == 256) return launch_decode_t<kF32, 256>(a, grid, lds, st);
+      break;
+    case kF16:
+      if (head_dim == 64) return launch_decode_t<kF16, 64>(a, grid, lds, st);
+      if (head_dim == 128) return launch_decode_t<kF16, 128>(a, grid, lds, st);
+      if (head_dim == 256) return launch_decode_t<kF16, 256>(a, grid, lds, st);
+      break;
+    case kBF16:
+      if (head_dim == 64) return launch_decode_t<kBF16, 64>(a, grid, lds, st);
+      if (head_dim == 128) return launch_decode_t<kBF16, 128>(a, grid, lds, st);
+      if (head_dim == 256) return launch_decode_t<kBF16, 256>(a, grid, lds, st);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st) {
+  switch (dtype) {
+    case kF32:
+      if (head_dim == 64) return launch_reduce_t<kF32, 64>(a, st);
+      if (head_dim == 128) return launch_reduce_t<kF32, 128>(a, st);
+      if (head_dim == 256) return launch_reduce_t<kF32, 256>(a, st);
+      break;
+    case kF16:
+      if (head_dim == 64) return launch_reduce_t<kF16, 64>(a, st);
+      if (head_dim == 128) return launch_reduce_t<kF16, 128>(a, st);
+      if (head_dim == 256) return launch_reduce_t<kF16, 256>(a, st);
+      break;
+    case kBF16:
+      if (head_dim == 64) return launch_reduce_t<kBF16, 64>(a, st);
+      if (head_dim == 128) return launch_reduce_t<kBF16, 128>(a, st);
+      if (head_dim == 256) return launch_reduce_t<kBF16, 256>(a, st);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t decode_groups_per_cu(int dtype, int head_dim, size_t lds, int* groups) {
+  switch (dtype) {
+    case kF32:
+      if (head_dim == 64) return occupancy_t<kF32, 64>(lds, groups);
+      if (head_dim == 128) return occupancy_t<kF32, 128>(lds, groups);
+      if (head_dim == 256) return occupancy_t<kF32, 256>(lds, groups);
+      break;
+    case kF16:
+      if (head_dim == 64) return occupancy_t<kF16, 64>(lds, groups);
+      if (head_dim == 128) return occupancy_t<kF16, 128>(lds, groups);
+      if (head_dim == 256) return occupancy_t<kF16, 256>(lds, groups);
+      break;
+    case kBF16:
+      if (head_dim == 64) return occupancy_t<kBF16, 64>(lds, groups);
+      if (head_dim == 128) return occupancy_t<kBF16, 128>(lds, groups);
+      if (head_dim == 256) return occupancy_t<kBF16, 256>(lds, groups);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

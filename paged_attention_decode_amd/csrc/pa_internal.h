@@ -1,0 +1,76 @@
+// Internal declarations shared by the libpagedattn translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+inline int elem_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+
+// Tokens per matrix-core tile: one 16x16 output tile covers 16 tokens.
+constexpr int kTile = 16;
+// Threads per workgroup of the attention kernel (four wave64 wavefronts).
+constexpr int kDecodeThreads = 256;
+constexpr int kWavesPerGroup = kDecodeThreads / 64;
+// Query heads handled together by one wavefront (columns of a 16x16 tile).
+constexpr int kHeadsPerTile = 16;
+// Largest batch: per-sequence tile prefix sums live in LDS (4 bytes each).
+constexpr int kMaxSeqs = 16383;
+// Balanced mode never gives a wavefront fewer tiles than this.
+constexpr int kMinTilesPerWave = 8;
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* ws_o;        // [num_waves][2][gh_max][head_dim] normalised partial outputs
+  float* ws_lse;      // [num_waves][2][gh_max] log2-sum-exp2 of each partial
+  int4* ws_meta;      // [num_seqs * segs_per_seq] {first wave, its slot, last wave, 0}
+  int64_t q_seq_stride;   // elements
+  int64_t num_blocks;
+  float scale_log2;       // scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;          // query heads per kv head
+  int32_t n_hg;           // ceil(group / 16): head groups per kv head
+  int32_t gh_max;         // min(group, 16)
+  int32_t segs_per_seq;   // num_kv_heads * n_hg
+  int32_t block_size;
+  int32_t bs_log2;
+  int32_t max_blocks;     // block table row length
+  int32_t out_f32;        // 1: fp32 output, 0: output in the input dtype
+  int32_t num_waves;      // wavefronts launched
+  int32_t range_tiles;    // >0 fixed tiles per wavefront, 0 balanced, -1 one pass
+};
+
+struct StoreArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int64_t k_stride;   // elements between tokens
+  int64_t v_stride;
+  int64_t num_slots;  // num_blocks * block_size
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+};
+
+// Launchers (return the launch error, hipSuccess otherwise).
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
+                         hipStream_t stream);
+hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t stream);
+// Resident workgroups of the attention kernel per compute unit for this LDS size.
+hipError_t decode_groups_per_cu(int dtype, int head_dim, size_t lds_bytes, int* groups);
+
+}  // namespace pa

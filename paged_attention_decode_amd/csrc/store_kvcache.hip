@@ -1,0 +1,73 @@
+// KV-cache scatter for gfx950: each decode step's new K/V rows are copied into
+// their cache slots (miniVLLM documentation, "What is miniVLLM?": paged KV
+// cache management). Bit copies, no conversion.
+//
+// One thread per (token, kv head, 16-byte chunk of the row). The K chunk maps
+// to one 16-byte run of the K page (layout [.. D/x][bs][x]); the V chunk's x
+// elements go to x separate dims of the V page (layout [.. bs/4][D][4]), each
+// at the token's position inside its group of four.
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+template <int E>
+__global__ __launch_bounds__(256) void store_kernel(const StoreArgs a) {
+  constexpr int kX = 16 / E;  // elements per 16-byte chunk
+  const int chunks = a.head_dim / kX;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)a.num_kv_heads * chunks;
+  if (idx >= (int64_t)a.num_tokens * per_token) return;
+  const int i = (int)(idx / per_token);
+  const int rem = (int)(idx - (int64_t)i * per_token);
+  const int g = rem / chunks;
+  const int c = rem - g * chunks;
+  const int64_t slot = a.slot_mapping[i];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot / a.block_size;
+  const int o = (int)(slot - blk * a.block_size);
+  const int64_t page = (blk * a.num_kv_heads + g) * (int64_t)a.block_size * a.head_dim;  // elements
+
+  const char* ksrc = reinterpret_cast<const char*>(a.k) + ((int64_t)i * a.k_stride + (int64_t)g * a.head_dim + (int64_t)c * kX) * E;
+  const char* vsrc = reinterpret_cast<const char*>(a.v) + ((int64_t)i * a.v_stride + (int64_t)g * a.head_dim + (int64_t)c * kX) * E;
+  const u4 kv = *reinterpret_cast<const u4*>(ksrc);
+  const u4 vv = *reinterpret_cast<const u4*>(vsrc);
+
+  char* kdst = reinterpret_cast<char*>(a.k_cache) + (page + ((int64_t)c * a.block_size + o) * kX) * E;
+  *reinterpret_cast<u4*>(kdst) = kv;
+
+  // V element (o, d) sits at [(o / 4) * D + d] * 4 + o % 4 within the page.
+  char* vpage = reinterpret_cast<char*>(a.v_cache) + page * E;
+  const int64_t vrow = (int64_t)(o >> 2) * a.head_dim * 4 + (o & 3);
+  if constexpr (E == 4) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vpage);
+#pragma unroll
+    for (int j = 0; j < kX; ++j) dst[vrow + (int64_t)(c * kX + j) * 4] = vv[j];
+  } else {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(vpage);
+#pragma unroll
+    for (int j = 0; j < kX; ++j) {
+      const uint32_t w = vv[j >> 1];
+      dst[vrow + (int64_t)(c * kX + j) * 4] = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t st) {
+  const int e = elem_bytes(dtype);
+  const int64_t threads = (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / (16 / e));
+  if (threads == 0) return hipSuccess;
+  const int64_t grid = (threads + 255) / 256;
+  if (e == 4)
+    hipLaunchKernelGGL(store_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(store_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

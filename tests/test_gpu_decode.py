@@ -1,0 +1,275 @@
+"""GPU parity: store_kvcache and paged_attention_decode through the C ABI against the CPU oracle.
+
+Tolerances (max-abs on fp32 output): 1e-5 for fp32 inputs, 2e-3 for fp16/bf16
+inputs. With output in the input dtype the bound is 2e-3 (or 1e-5) plus half
+an ulp of that dtype at the oracle value: one final round-to-nearest-even.
+The scatter must be bit-exact over the whole cache buffers.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import CONFIG_ORDER, get_config, make_inputs, nan_of, poison_blocks
+from _gpu_helpers import (TOL, custom_config, geometry, half_ulp, np_to_torch, oracle_after_store, to_device,
+                          torch_dtype, torch_to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run_step(dev, x, partition_size=0, out_dtype=None):
+    import torch
+    import paged_attention_decode_amd as pa
+    pa.store_kvcache(dev["k_new"], dev["v_new"], dev["slot_mapping"], dev["k_cache"], dev["v_cache"])
+    out = pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                    dev["context_lens"], x.scale, out_dtype=out_dtype or torch.float32,
+                                    partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out
+
+
+def _sample_seqs(x, limit):
+    """All sequences if few, else the shortest, the longest and a seeded random rest, ``limit`` in all."""
+    b = x.cfg.batch
+    if b <= limit:
+        return list(range(b))
+    order = np.argsort(x.context_lens, kind="stable")
+    ends = max(1, min(4, limit // 4))
+    pick = list(dict.fromkeys(order[:ends].tolist() + order[-ends:].tolist()))[:limit]
+    rest = [s for s in np.random.default_rng(0).permutation(b).tolist() if s not in pick]
+    return sorted(pick + rest[:limit - len(pick)])
+
+
+_CACHE = {}
+
+
+def _inputs(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        _CACHE[name] = make_inputs(get_config(name))
+    return _CACHE[name]
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_full_config_store_bit_exact_and_decode_parity(cuda, name):
+    """Every workload at full size, default launch (the one the bench times)."""
+    import torch
+    _say(f"[gpu] full config {name}: generating")
+    x = _inputs(name)
+    limit = {"long_ctx_bf16": 3, "skewed_prefix_bf16": 40}.get(name, 10 ** 9)
+    seqs = _sample_seqs(x, limit)
+    dev = to_device(x, cuda)
+    _say(f"[gpu] full config {name}: store + decode, B={x.cfg.batch}")
+    out = _run_step(dev, x).cpu().numpy()
+    k2, v2, ref = oracle_after_store(x, seqs=seqs)
+    assert torch_to_np(dev["k_cache"], x.cfg.dtype).reshape(-1).tobytes() == k2.reshape(-1).tobytes()
+    assert torch_to_np(dev["v_cache"], x.cfg.dtype).reshape(-1).tobytes() == v2.reshape(-1).tobytes()
+    assert np.isfinite(out).all()
+    err = np.abs(out[seqs] - ref[seqs]).max()
+    _say(f"[gpu] {name}: max-abs error {err:.3e} over {len(seqs)} sequences")
+    assert err <= TOL[x.cfg.dtype]
+    # the same step with output in the input dtype: one extra rounding at most
+    if x.cfg.dtype != "fp32":
+        out_t = _run_step(dev, x, out_dtype=torch_dtype(x.cfg.dtype)).float().cpu().numpy()
+        bound = TOL[x.cfg.dtype] + half_ulp(ref[seqs], x.cfg.dtype)
+        assert (np.abs(out_t[seqs] - ref[seqs]) <= bound).all()
+    del dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("psize", [-1, 0, 16, 48, 512])
+@pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"])
+def test_launch_modes_agree_with_oracle(cuda, name, psize):
+    _say(f"[gpu] modes {name} partition_size={psize}")
+    x = _inputs(name)
+    dev = to_device(x, cuda)
+    out = _run_step(dev, x, partition_size=psize).cpu().numpy()
+    _, _, ref = oracle_after_store(x)
+    assert np.abs(out - ref).max() <= TOL[x.cfg.dtype]
+
+
+CASES = [
+    # dtype, batch, Hq, Hkv, D, bs, lengths
+    ("bf16", 5, 8, 2, 128, 16, (1, 2, 15, 16, 17)),
+    ("fp16", 4, 4, 4, 64, 32, (31, 32, 33, 95)),
+    ("fp32", 3, 6, 2, 128, 16, (5, 40, 77)),
+    ("bf16", 3, 40, 2, 64, 16, (50, 1, 130)),          # 20 heads per kv head: groups of 16 + 4
+    ("fp16", 2, 3, 1, 256, 64, (200, 63)),             # odd group, head_dim 256
+    ("bf16", 4, 16, 2, 256, 256, (300, 256, 257, 1)),
+    ("fp32", 2, 8, 1, 64, 128, (129, 300)),
+    ("bf16", 6, 8, 8, 128, 16, (0, 5, 0, 64, 3, 1)),   # empty contexts give zeros
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("psize", [-1, 0, 16, 64])
+def test_small_shapes_and_edges(cuda, case, psize):
+    dt, b, hq, hkv, d, bs, lens = CASES[case]
+    _say(f"[gpu] small case {CASES[case]} partition_size={psize}")
+    x = make_inputs(custom_config(dtype=dt, batch=b, hq=hq, hkv=hkv, d=d, bs=bs, lens=lens, seed=100 + case))
+    # context length 0 has no token to store: skip its slot
+    x.slot_mapping[x.context_lens == 0] = -1
+    dev = to_device(x, cuda)
+    out = _run_step(dev, x, partition_size=psize).cpu().numpy()
+    k2, v2, ref = oracle_after_store(x)
+    assert torch_to_np(dev["k_cache"], dt).reshape(-1).tobytes() == k2.reshape(-1).tobytes()
+    assert np.abs(out - ref).max() <= TOL[dt]
+    for s in np.flatnonzero(x.context_lens == 0):
+        assert (out[s] == 0).all()
+
+
+def test_length_one_returns_value_row_exactly(cuda):
+    import torch
+    import paged_attention_decode_amd as pa
+    x = make_inputs(custom_config(dtype="bf16", batch=4, hq=8, hkv=2, lens=(1, 1, 1, 1), seed=3))
+    dev = to_device(x, cuda)
+    for psize in (-1, 0):
+        out = _run_step(dev, x, partition_size=psize).cpu().numpy()
+        k2, v2, _ = oracle_after_store(x)
+        geo = geometry(x)
+        for s in range(4):
+            _, v = oracle.gather_kv(k2, v2, x.block_tables[s], 1, geo)
+            for h in range(8):
+                np.testing.assert_array_equal(out[s, h], v[0, h // 4])
+
+
+def test_identical_keys_give_mean_of_values(cuda):
+    import torch
+    import paged_attention_decode_amd as pa
+    x = make_inputs(custom_config(dtype="bf16", batch=2, hq=8, hkv=2, lens=(77, 300), seed=4))
+    geo = geometry(x)
+    # one key row repeated over every slot of both caches' K (identical keys for every token)
+    k = x.k_cache.reshape(geo.k_shape).copy()
+    k[...] = k[:1, :, :, :1, :]
+    x.k_cache = k.reshape(-1)
+    x.slot_mapping[:] = -1
+    dev = to_device(x, cuda)
+    out = _run_step(dev, x).cpu().numpy()
+    for s in range(2):
+        _, v = oracle.gather_kv(x.k_cache, x.v_cache, x.block_tables[s], int(x.context_lens[s]), geo)
+        mean = v.mean(axis=0)
+        for h in range(8):
+            assert np.abs(out[s, h] - mean[h // 4]).max() <= 2e-3
+
+
+def test_poisoned_tail_slots_and_unused_blocks_change_nothing(cuda):
+    """NaN in slots past each context and in unreferenced blocks must not reach the output."""
+    cfg = custom_config(dtype="bf16", batch=5, hq=8, hkv=2, lens=(3, 17, 250, 33, 1), seed=5)
+    x = make_inputs(cfg)
+    x.slot_mapping[:] = -1
+    geo = geometry(x)
+    clean = {p: _run_step(to_device(x, cuda), x, partition_size=p).cpu().numpy() for p in (-1, 0, 16)}
+    kp = poison_blocks(x.k_cache, x.unused_blocks, cfg)
+    vp = poison_blocks(x.v_cache, x.unused_blocks, cfg)
+    # tail slots of each sequence's last block, written with NaN rows by the oracle's scatter
+    bs = cfg.block_size
+    tail = []
+    for s in range(cfg.batch):
+        L = int(x.context_lens[s])
+        blk = int(x.block_tables[s, (L - 1) // bs])
+        tail += [blk * bs + o for o in range(L % bs or bs, bs)]
+    nan_rows = np.full((len(tail), cfg.num_kv_heads, cfg.head_dim), nan_of("bf16"), dtype=np.uint16)
+    kp, vp = oracle.store_kvcache(nan_rows, nan_rows, np.array(tail, np.int32), kp, vp, geo)
+    x.k_cache, x.v_cache = kp, vp
+    for p, ref in clean.items():
+        out = _run_step(to_device(x, cuda), x, partition_size=p).cpu().numpy()
+        assert out.tobytes() == ref.tobytes(), f"partition_size={p}"
+
+
+def test_relabelling_physical_blocks_is_bit_identical(cuda):
+    cfg = custom_config(dtype="fp16", batch=4, hq=16, hkv=4, d=64, lens=(100, 7, 64, 513), seed=6)
+    x = make_inputs(cfg)
+    x.slot_mapping[:] = -1
+    out = _run_step(to_device(x, cuda), x).cpu().numpy()
+    geo = geometry(x)
+    pi = np.random.default_rng(1).permutation(x.num_blocks)
+    for name in ("k_cache", "v_cache"):
+        a = getattr(x, name).reshape(geo.num_blocks, -1)
+        b = np.empty_like(a)
+        b[pi] = a
+        setattr(x, name, b.reshape(-1))
+    x.block_tables = pi[x.block_tables].astype(np.int32)
+    out2 = _run_step(to_device(x, cuda), x).cpu().numpy()
+    assert out.tobytes() == out2.tobytes()
+
+
+def test_repeat_runs_are_deterministic(cuda):
+    x = _inputs("llama32_1b_fp16")
+    dev = to_device(x, cuda)
+    a = _run_step(dev, x).cpu().numpy()
+    b = _run_step(dev, x).cpu().numpy()
+    assert a.tobytes() == b.tobytes()
+
+
+def test_strided_q_and_k_v_slices(cuda):
+    """q, k and v taken as column slices of one fused projection output."""
+    import torch
+    import paged_attention_decode_amd as pa
+    cfg = custom_config(dtype="bf16", batch=3, hq=8, hkv=2, lens=(40, 1, 90), seed=8)
+    x = make_inputs(cfg)
+    dev = to_device(x, cuda)
+    b, hq, hkv, d = 3, 8, 2, 128
+    fused = torch.zeros(b, (hq + 2 * hkv) * d, dtype=torch.bfloat16, device=cuda)
+    fused[:, :hq * d] = dev["q"].reshape(b, -1)
+    fused[:, hq * d:(hq + hkv) * d] = dev["k_new"].reshape(b, -1)
+    fused[:, (hq + hkv) * d:] = dev["v_new"].reshape(b, -1)
+    q = fused[:, :hq * d].view(b, hq, d)
+    k = fused[:, hq * d:(hq + hkv) * d].view(b, hkv, d)
+    v = fused[:, (hq + hkv) * d:].view(b, hkv, d)
+    assert q.stride(0) == (hq + 2 * hkv) * d
+    pa.store_kvcache(k, v, dev["slot_mapping"], dev["k_cache"], dev["v_cache"])
+    out = pa.paged_attention_decode(q, dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                                    x.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    k2, v2, ref = oracle_after_store(x)
+    assert torch_to_np(dev["k_cache"], "bf16").reshape(-1).tobytes() == k2.reshape(-1).tobytes()
+    assert np.abs(out.cpu().numpy() - ref).max() <= 2e-3
+
+
+def test_store_skips_negative_and_out_of_range_slots(cuda):
+    import torch
+    import paged_attention_decode_amd as pa
+    cfg = custom_config(dtype="fp16", batch=4, hq=4, hkv=2, d=64, lens=(5, 9, 12, 3), seed=9)
+    x = make_inputs(cfg)
+    nslots = x.num_blocks * cfg.block_size
+    x.slot_mapping = np.array([x.slot_mapping[0], -1, nslots, x.slot_mapping[3]], np.int32)
+    dev = to_device(x, cuda)
+    pa.store_kvcache(dev["k_new"], dev["v_new"], dev["slot_mapping"], dev["k_cache"], dev["v_cache"])
+    torch.cuda.synchronize()
+    geo = geometry(x)
+    sm = x.slot_mapping.copy()
+    sm[2] = -1
+    k2, v2 = oracle.store_kvcache(x.k_new, x.v_new, sm, x.k_cache, x.v_cache, geo)
+    assert torch_to_np(dev["k_cache"], "fp16").reshape(-1).tobytes() == k2.reshape(-1).tobytes()
+    assert torch_to_np(dev["v_cache"], "fp16").reshape(-1).tobytes() == v2.reshape(-1).tobytes()
+
+
+def test_caller_workspace_and_events(cuda):
+    import torch
+    import paged_attention_decode_amd as pa
+    x = _inputs("qwen3_0p6b_bf16")
+    c = x.cfg
+    dev = to_device(x, cuda)
+    need = pa.workspace_bytes(c.batch, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
+                              c.max_blocks_per_seq, pa.DTYPE_BF16, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=cuda)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    out = pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                    dev["context_lens"], x.scale, out_dtype=torch.float32, workspace=ws, events=ev)
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0
+    ref = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, x.scale, geometry(x))
+    assert np.abs(out.cpu().numpy() - ref).max() <= 2e-3
+    with pytest.raises(pa.PagedAttnError) as ei:
+        pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                  dev["context_lens"], x.scale, workspace=ws[:need // 2])
+    assert ei.value.code == 5
