@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "skewed_prefix_bf16"
 KERNEL_SOURCE = ROOT / "paged_attention_decode_amd" / "csrc" / "decode.hip"
 PROFILES = ROOT / "profiles"
+COPY_BYTES = 256 << 20
 
 
 def parse():
@@ -50,6 +51,15 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="target seconds of oracle work")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/decode_<workload>_traffic.txt from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, then WRITE_SIZE) of this script, then exit")
+    ap.add_argument("--pmc-commands", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("", ""),
+                    help="the two profiling commands, recorded in the summary")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write profiles/decode_<workload>_kernel_trace.txt from a rocprofv3 --kernel-trace "
+                         "--stats run of this script, then exit")
+    ap.add_argument("--trace-command", default="", help="the profiling command, recorded in the summary")
     return ap.parse_args()
 
 
@@ -75,6 +85,82 @@ def traffic_from_profiles(workload: str, launches_bytes: float):
         return None
 
 
+def _pmc_rows(directory: str, counter: str):
+    import csv
+    files = sorted(Path(directory).rglob("*counter_collection.csv"))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(workload: str, fetch_dir: str, write_dir: str, commands) -> Path:
+    """HBM bytes per attention-kernel launch, with FETCH/WRITE_SIZE scaled by a copy of known size."""
+    out = {}
+    for key, directory, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(directory, counter)
+        dec = [v for n, v in rows if "decode_kernel" in n]
+        # the largest copy kernel in the run is the device-to-device copy of COPY_BYTES
+        cpy = [v for n, v in rows if "copy" in n.lower()]
+        if not dec or not cpy:
+            raise SystemExit(f"{counter}: decode or copy kernel missing in {directory}")
+        out[key] = (sum(dec) / len(dec), max(cpy), len(dec))
+    known_kib = COPY_BYTES / 1024.0
+    f_fetch = known_kib / out["fetch"][1]
+    f_write = known_kib / out["write"][1]
+    fetch_b = out["fetch"][0] * f_fetch * 1024.0
+    write_b = out["write"][0] * f_write * 1024.0
+    path = PROFILES / f"decode_{workload}_traffic.txt"
+    PROFILES.mkdir(exist_ok=True)
+    path.write_text("\n".join([
+        f"# HBM traffic of the attention kernel (decode_kernel) on workload {workload}",
+        "# from two rocprofv3 --pmc runs of bench.py; FETCH_SIZE / WRITE_SIZE are KiB per dispatch,",
+        f"# scaled by the same counter on a plain {COPY_BYTES >> 20} MiB copy kernel in the same run",
+        f"# fetch command: {commands[0]}",
+        f"# write command: {commands[1]}",
+        f"# summary command: python bench.py --workload {workload} --summarize-pmc {fetch_dir} {write_dir}",
+        f"kernel_source_sha256: {kernel_source_sha()}",
+        f"decode_dispatches: {out['fetch'][2]}",
+        f"fetch_kib_per_dispatch_raw: {out['fetch'][0]:.1f}",
+        f"write_kib_per_dispatch_raw: {out['write'][0]:.1f}",
+        f"copy_fetch_kib_raw: {out['fetch'][1]:.1f}",
+        f"copy_write_kib_raw: {out['write'][1]:.1f}",
+        f"copy_factor_fetch: {f_fetch:.4f}",
+        f"copy_factor_write: {f_write:.4f}",
+        f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"hbm_write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+    ]) + "\n")
+    return path
+
+
+def summarize_trace(workload: str, directory: str, command: str) -> Path:
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace --stats run, as text."""
+    import csv
+    files = sorted(Path(directory).rglob("*kernel_stats.csv"))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {directory}")
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+             f"# command: {command}",
+             f"# summary command: python bench.py --workload {workload} --summarize-trace {directory}",
+             f"kernel_source_sha256: {kernel_source_sha()}",
+             f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+    for r in csv.DictReader(open(files[0])):
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        name = name if len(name) <= 72 else name[:69] + "..."
+        lines.append(f"{name:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    path = PROFILES / f"decode_{workload}_kernel_trace.txt"
+    PROFILES.mkdir(exist_ok=True)
+    path.write_text("\n".join(lines) + "\n")
+    return path
+
+
 def describe(cfg) -> dict:
     lens = {"list": f"{list(cfg.len_list)}", "fixed": f"all {cfg.len_hi}",
             "uniform": f"uniform [{cfg.len_lo}, {cfg.len_hi}]",
@@ -98,32 +184,35 @@ def cpu_baseline(x, gpu_out, budget_s: float) -> dict:
     c = x.cfg
     geo = oracle.CacheGeometry(x.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.dtype)
     k2, v2 = oracle.store_kvcache(x.k_new, x.v_new, x.slot_mapping, x.k_cache, x.v_cache, geo)
-    # pick sequences in a seeded order until the estimated work fills the budget
-    order = np.random.default_rng(12345).permutation(c.batch)
-    probe = order[:1].tolist()
-    t = time.perf_counter()
-    oracle.decode(x.q, k2, v2, x.block_tables, x.context_lens, x.scale, geo, seqs=probe)
-    per_token = (time.perf_counter() - t) / max(1, int(x.context_lens[probe].sum()))
-    seqs, tokens = [], 0
-    for s in order:
-        seqs.append(int(s))
-        tokens += int(x.context_lens[s])
-        if tokens * per_token >= budget_s:
-            break
-    t = time.perf_counter()
-    ref = oracle.decode(x.q, k2, v2, x.block_tables, x.context_lens, x.scale, geo, seqs=seqs)
-    dt = time.perf_counter() - t
+    # sequences in a seeded order, in chunks, until the time budget is spent or the batch is done
+    order = np.random.default_rng(12345).permutation(c.batch).tolist()
+    seqs, tokens, dt = [], 0, 0.0
+    ref = np.zeros((c.batch, c.num_heads, c.head_dim))
+    while order and dt < budget_s:
+        chunk, order = order[:8], order[8:]
+        t = time.perf_counter()
+        part = oracle.decode(x.q, k2, v2, x.block_tables, x.context_lens, x.scale, geo, seqs=chunk)
+        dt += time.perf_counter() - t
+        ref[chunk] = part[chunk]
+        seqs += chunk
+        tokens += int(x.context_lens[chunk].sum())
     kv = tokens * c.num_kv_heads * c.head_dim * c.elem_bytes * 2
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     err = float(np.abs(gpu_out[seqs] - ref[seqs]).max())
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(seqs)} of {c.batch} sequences ({tokens} context tokens), float64 numpy, one pass",
+            "sample": f"{len(seqs)} of {c.batch} sequences ({tokens} context tokens) after the step's scatter, float64 numpy",
             "seconds": dt, "tokens_per_s": len(seqs) / dt, "host_cpus": len(os.sched_getaffinity(0)),
             "parity_max_abs_err_vs_gpu": err}
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        print(summarize_pmc(args.workload, args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.workload, args.summarize_trace, args.trace_command))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the decode "
@@ -168,6 +257,13 @@ def main():
         pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
                                   partition_size=args.partition_size, workspace=ws, events=events)
 
+    # A plain copy of known size (COPY_BYTES read + written): counter runs scale HBM bytes by it.
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -198,9 +294,10 @@ def main():
     # Steps timed after overwriting 1 GiB, so last-level caches hold no KV (reported beside the main figure).
     cold = []
     if args.cold_steps > 0:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # reading (not writing) 1 GiB leaves no dirty lines to be written back during the step
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         for _ in range(args.cold_steps):
-            scratch.fill_(1)
+            scratch.sum()
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             step(ev)
             torch.cuda.synchronize()

@@ -417,54 +417,84 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 }
 
 // Merge of the pieces of every cut segment: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),
-// M = max_p lse_p, pieces taken in wavefront order (deterministic).
+// M = max_p lse_p. One wavefront per (segment, head): lane p holds piece p's lse, the pieces'
+// output rows are read eight at a time so their loads are in flight together. Summation order
+// is fixed (deterministic).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   constexpr int kPer = D / 64;
+  constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63;
-  const int seg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int seg = (int)(item / a.gh_max);
+  const int n = (int)(item - (int64_t)seg * a.gh_max);
   if (seg >= a.num_seqs * a.segs_per_seq) return;
+  const int r = seg % a.segs_per_seq;
+  const int g = r / a.n_hg;
+  const int hg = r - g * a.n_hg;
+  const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
+  if (n >= gh) return;
   const int4 meta = a.ws_meta[seg];
   const int wa = meta.x, slot_a = meta.y, wb = meta.z;
   if (wb <= wa) return;  // finished inside one wavefront
-  const int s = seg / a.segs_per_seq;
-  const int r = seg - s * a.segs_per_seq;
-  const int g = r / a.n_hg;
-  const int hg = r - g * a.n_hg;
-  const int h0 = g * a.group + hg * kHeadsPerTile;
-  const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
-  for (int n = 0; n < gh; ++n) {
-    float M = -INFINITY;
-    for (int w = wa; w <= wb; ++w) {
-      const int sl = (w == wa) ? slot_a : 0;
-      M = fmaxf(M, a.ws_lse[((int64_t)w * 2 + sl) * a.gh_max + n]);
+  const int np = wb - wa + 1;
+  // Workspace row of piece p: wavefront wa + p, slot slot_a for the first piece, 0 after it.
+  auto row_of = [&](int p) -> int64_t {
+    return ((int64_t)(wa + p) * 2 + (p == 0 ? slot_a : 0)) * a.gh_max + n;
+  };
+  float M = -INFINITY;
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const int p = p0 + lane;
+    if (p < np) M = fmaxf(M, a.ws_lse[row_of(p)]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float acc[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
+  float wsum = 0.f;
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const int p = p0 + lane;
+    float wl = 0.f;
+    if (p < np) {
+      const float x = a.ws_lse[row_of(p)];
+      wl = (x == -INFINITY) ? 0.f : exp2_fast(x - M);
     }
-    float accv[kPer];
+    wsum += wl;
+    const int cnt = min(64, np - p0);
+    for (int k0 = 0; k0 < cnt; k0 += kBatch) {
+      float vals[kBatch][kPer];
+      float wk[kBatch];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) accv[k] = 0.f;
-    float wsum = 0.f;
-    for (int w = wa; w <= wb; ++w) {
-      const int sl = (w == wa) ? slot_a : 0;
-      const int64_t row = ((int64_t)w * 2 + sl) * a.gh_max + n;
-      const float x = a.ws_lse[row];
-      const float wt = (x == -INFINITY) ? 0.f : exp2_fast(x - M);
-      wsum += wt;
-      const float* o = a.ws_o + row * D + lane * kPer;
+      for (int b = 0; b < kBatch; ++b) {
+        const int k = min(k0 + b, cnt - 1);
+        wk[b] = (k0 + b < cnt) ? __shfl(wl, k) : 0.f;
+        const float* o = a.ws_o + row_of(p0 + k) * D + lane * kPer;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) accv[k] += wt * o[k];
-    }
-    const float inv = 1.0f / wsum;
-    const int64_t obase = ((int64_t)s * a.num_heads + h0 + n) * D + lane * kPer;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const float v = accv[k] * inv;
-      if (a.out_f32) {
-        reinterpret_cast<float*>(a.out)[obase + k] = v;
-      } else if constexpr (DT == kBF16) {
-        reinterpret_cast<uint16_t*>(a.out)[obase + k] = (uint16_t)bf16_bits_rne(v);
-      } else if constexpr (DT == kF16) {
-        reinterpret_cast<_Float16*>(a.out)[obase + k] = (_Float16)v;
+        for (int j = 0; j < kPer; ++j) vals[b][j] = o[j];
       }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) acc[j] += wk[b] * vals[b][j];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+  const float inv = 1.0f / wsum;
+  const int s = seg / a.segs_per_seq;
+  const int h0 = g * a.group + hg * kHeadsPerTile;
+  const int64_t obase = ((int64_t)s * a.num_heads + h0 + n) * D + lane * kPer;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const float v = acc[k] * inv;
+    if (a.out_f32) {
+      reinterpret_cast<float*>(a.out)[obase + k] = v;
+    } else if constexpr (DT == kBF16) {
+      reinterpret_cast<uint16_t*>(a.out)[obase + k] = (uint16_t)bf16_bits_rne(v);
+    } else if constexpr (DT == kF16) {
+      reinterpret_cast<_Float16*>(a.out)[obase + k] = (_Float16)v;
     }
   }
 }
@@ -477,8 +507,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, int grid, size_t lds, hipStream_
 
 template <int DT, int D>
 hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
-  const int nseg = a.num_seqs * a.segs_per_seq;
-  hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((nseg + 3) / 4), dim3(256), 0, st, a);
+  const int64_t items = (int64_t)a.num_seqs * a.segs_per_seq * a.gh_max;
+  hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
