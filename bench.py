@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--partition-size", type=int, default=0, help="0 balanced split, -1 one pass, >0 fixed")
+    ap.add_argument("--cached-prefix-tokens", type=int, default=0,
+                    help="leading tokens per context read with cached loads (0 library default, -1 none)")
     ap.add_argument("--cold-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="target seconds of oracle work")
@@ -255,7 +257,8 @@ def main():
     def step(events=None):
         pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache)
         pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
-                                  partition_size=args.partition_size, workspace=ws, events=events)
+                                  partition_size=args.partition_size,
+                                  cached_prefix_tokens=args.cached_prefix_tokens, workspace=ws, events=events)
 
     # A plain copy of known size (COPY_BYTES read + written): counter runs scale HBM bytes by it.
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -310,7 +313,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the workload)",
         "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
-                       partition_size=args.partition_size, parallelism="single GPU"),
+                       partition_size=args.partition_size, cached_prefix_tokens=args.cached_prefix_tokens,
+                       parallelism="single GPU"),
         "tokens_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -168,6 +168,14 @@ int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_
  *       wavefront; no reduce kernel runs.
  *   >0  fixed ranges of partition_size tokens (a multiple of 16) over the same
  *       concatenated tile stream.
+ * cached_prefix_tokens: K/V of the first cached_prefix_tokens tokens of every
+ *       context are read with the default cache policy; later tokens are read
+ *       with the non-temporal (streaming) policy, which moves single-use data
+ *       faster but does not keep it in the last-level cache. Prefix caching
+ *       shares the leading blocks of contexts between sequences, so those are
+ *       the reads worth keeping. 0 = library default
+ *       (PA_DEFAULT_CACHED_PREFIX_TOKENS), -1 = stream everything, INT32_MAX =
+ *       never stream. Changes speed only, never results.
  * workspace / workspace_bytes: device memory used instead of the library's own
  *       (NULL = library-owned). Must be 256-byte aligned and at least
  *       pa_decode_workspace_bytes(...) bytes. Its contents need no
@@ -176,9 +184,11 @@ int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_
  *       `stream` immediately before and after the attention kernel itself (not
  *       the reduce kernel), so callers can time that kernel alone.
  */
+#define PA_DEFAULT_CACHED_PREFIX_TOKENS 1024
+
 typedef struct pa_decode_opts {
   int32_t partition_size;
-  int32_t reserved;
+  int32_t cached_prefix_tokens;
   void* workspace;
   size_t workspace_bytes;
   void* event_begin;

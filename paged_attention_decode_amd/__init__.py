@@ -21,6 +21,7 @@ them and ``k_cache_shape`` / ``v_cache_shape`` give the shapes:
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 from typing import Optional, Tuple
 
@@ -30,7 +31,8 @@ __all__ = [
     "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16",
 ]
 
-_LIB_PATH = Path(__file__).resolve().with_name("libpagedattn.so")
+# PAGEDATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
+_LIB_PATH = Path(os.environ.get("PAGEDATTN_LIBRARY") or Path(__file__).resolve().with_name("libpagedattn.so"))
 _lib = None
 
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
@@ -47,7 +49,7 @@ class PagedAttnError(RuntimeError):
 class DecodeOpts(ctypes.Structure):
     _fields_ = [
         ("partition_size", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("cached_prefix_tokens", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("event_begin", ctypes.c_void_p),
@@ -176,11 +178,14 @@ def store_kvcache(k, v, slot_mapping, k_cache, v_cache) -> None:
 
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
-                           out_dtype=None, partition_size: int = 0, workspace=None, events=None):
+                           out_dtype=None, partition_size: int = 0, cached_prefix_tokens: int = 0,
+                           workspace=None, events=None):
     """Decode attention; returns ``out`` ([B, Hq, D], fp32 or q's dtype).
 
     partition_size: 0 balanced split (default), -1 one pass per sequence,
-    >0 fixed ranges of that many tokens. workspace: optional uint8 CUDA tensor
+    >0 fixed ranges of that many tokens. cached_prefix_tokens: leading tokens
+    of each context read with cached loads, the rest streamed (0 library
+    default, -1 stream all; speed only). workspace: optional uint8 CUDA tensor
     (see ``workspace_bytes``). events: optional (begin, end) torch.cuda.Event
     pair recorded around the attention kernel itself.
     """
@@ -206,6 +211,7 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         raise ValueError("out must be a contiguous [B, Hq, D] tensor")
     opts = DecodeOpts()
     opts.partition_size = int(partition_size)
+    opts.cached_prefix_tokens = int(cached_prefix_tokens)
     if workspace is not None:
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()

@@ -318,6 +318,10 @@ int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void*
   a.out_f32 = out_dtype == PA_DTYPE_F32 ? 1 : 0;
   a.num_waves = (int32_t)p.num_waves;
   a.range_tiles = p.range_tiles;
+  {
+    const int32_t hint = opts ? opts->cached_prefix_tokens : 0;
+    a.cached_prefix_tokens = hint == 0 ? PA_DEFAULT_CACHED_PREFIX_TOKENS : (hint < 0 ? 0 : hint);
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (opts && opts->event_begin) {

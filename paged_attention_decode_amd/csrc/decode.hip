@@ -35,6 +35,20 @@
 
 #include <math.h>
 
+// Cache policy of the K/V page loads (gfx940-family buffer instruction bits):
+// tiles at or past DecodeArgs::cached_prefix_tokens are loaded non-temporal
+// (streamed through the caches); earlier tiles, where prefix-cached blocks
+// shared between sequences live, use the default policy so sequences sharing
+// them can hit in the last-level cache.
+constexpr int kPolicyDefault = 0;
+constexpr int kPolicyStream = 2;  // nt
+// Third descriptor word of a raw 32-bit buffer resource on gfx9-family GPUs.
+constexpr int kRsrcWord3 = 0x00020000;
+// Tiles whose K/V loads are in flight ahead of the tile being computed (1 or 2).
+#ifndef PA_PREFETCH_TILES
+#define PA_PREFETCH_TILES 1
+#endif
+
 namespace pa {
 namespace {
 
@@ -53,6 +67,8 @@ struct Cfg {
   static constexpr int kChunks = D / kX;           // 16-byte chunks per key row
   static constexpr int kLoads = kChunks / 4;       // 16-byte loads per lane per tile (K, and V)
   static constexpr int kAcc = D / 16;              // 16x16 accumulator tiles of O^T
+  // Deeper prefetch only where the extra register set still fits two wavefronts per SIMD.
+  static constexpr int kPrefetch = (PA_PREFETCH_TILES >= 2 && kLoads <= 4) ? 2 : 1;
 };
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
@@ -62,6 +78,16 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte load at byte `off` of a buffer resource, with cache policy POL.
+template <int POL>
+__device__ __forceinline__ u4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kRsrcWord3);
+}
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) {
   return L < 0 ? 0 : (L > max_len ? max_len : L);
@@ -124,6 +150,7 @@ struct Piece {
 
     if (L > 0) {
       const int64_t page_bytes = (int64_t)bs * D * C::kE;
+      const int page_bytes32 = (int)page_bytes;
       const int64_t blk_stride = (int64_t)a.num_kv_heads * page_bytes;
       const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * page_bytes;
       const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * page_bytes;
@@ -150,14 +177,23 @@ struct Piece {
         }
         int64_t blk = __builtin_amdgcn_readlane(bt_val, page - bt_first);
         blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
-        const char* kp = kbase + blk * blk_stride + off0 * 16;
-        const char* vp = vbase + blk * blk_stride + (int64_t)off0 * D * C::kE;
+        // One buffer resource per page: the page's base in scalar registers,
+        // 32-bit lane offsets, and loads past the page end return zero.
+        const __amdgpu_buffer_rsrc_t kr = page_rsrc(kbase + blk * blk_stride, page_bytes32);
+        const __amdgpu_buffer_rsrc_t vr = page_rsrc(vbase + blk * blk_stride, page_bytes32);
+        const int koff = (int)k_lane + off0 * 16;
+        const int voff = (int)v_lane + off0 * D * C::kE;
+        if (t0 >= a.cached_prefix_tokens) {
 #pragma unroll
-        for (int j = 0; j < C::kLoads; ++j)
-          kb[j] = *reinterpret_cast<const u4*>(kp + k_lane + j * 64 * bs);
+          for (int j = 0; j < C::kLoads; ++j) kb[j] = buf_load16<kPolicyStream>(kr, koff + j * 64 * bs);
 #pragma unroll
-        for (int j = 0; j < C::kLoads; ++j)
-          vb[j] = *reinterpret_cast<const u4*>(vp + v_lane + j * 256);
+          for (int j = 0; j < C::kLoads; ++j) vb[j] = buf_load16<kPolicyStream>(vr, voff + j * 256);
+        } else {
+#pragma unroll
+          for (int j = 0; j < C::kLoads; ++j) kb[j] = buf_load16<kPolicyDefault>(kr, koff + j * 64 * bs);
+#pragma unroll
+          for (int j = 0; j < C::kLoads; ++j) vb[j] = buf_load16<kPolicyDefault>(vr, voff + j * 256);
+        }
       };
 
       auto compute_tile = [&](int i, const u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
@@ -257,6 +293,25 @@ struct Piece {
         }
       };
 
+      if constexpr (C::kPrefetch >= 2) {
+      // Three register sets in rotation: tiles i+1 and i+2 are in flight while tile i is computed.
+      u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads], kC[C::kLoads], vC[C::kLoads];
+      int i = lt0;
+      load_tile(i, kA, vA);
+      if (i + 1 < lt1) load_tile(i + 1, kB, vB);
+      while (true) {
+        if (i + 2 < lt1) load_tile(i + 2, kC, vC);
+        compute_tile(i, kA, vA);
+        if (i + 1 >= lt1) break;
+        if (i + 3 < lt1) load_tile(i + 3, kA, vA);
+        compute_tile(i + 1, kB, vB);
+        if (i + 2 >= lt1) break;
+        if (i + 4 < lt1) load_tile(i + 4, kB, vB);
+        compute_tile(i + 2, kC, vC);
+        if (i + 3 >= lt1) break;
+        i += 3;
+      }
+      } else {
       // Two register sets: the loads of tile i+1 are in flight while tile i is computed.
       u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads];
       int i = lt0;
@@ -271,6 +326,7 @@ struct Piece {
         compute_tile(i + 1, kB, vB);
         if (!has_a) break;
         i += 2;
+      }
       }
     }
 

@@ -48,6 +48,7 @@ struct DecodeArgs {
   int32_t out_f32;        // 1: fp32 output, 0: output in the input dtype
   int32_t num_waves;      // wavefronts launched
   int32_t range_tiles;    // >0 fixed tiles per wavefront, 0 balanced, -1 one pass
+  int32_t cached_prefix_tokens;  // tiles starting before this token use cached loads, later ones stream
 };
 
 struct StoreArgs {
