@@ -20,7 +20,10 @@ constexpr int kHeadsPerTile = 16;
 // Largest batch: per-sequence tile prefix sums live in LDS (4 bytes each).
 constexpr int kMaxSeqs = 16383;
 // Balanced mode never gives a wavefront fewer tiles than this.
-constexpr int kMinTilesPerWave = 8;
+#ifndef PA_MIN_TILES_PER_WAVE
+#define PA_MIN_TILES_PER_WAVE 2
+#endif
+constexpr int kMinTilesPerWave = PA_MIN_TILES_PER_WAVE;
 
 struct DecodeArgs {
   const void* q;
