@@ -273,3 +273,49 @@ def test_caller_workspace_and_events(cuda):
         pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                                   dev["context_lens"], x.scale, workspace=ws[:need // 2])
     assert ei.value.code == 5
+
+
+@pytest.mark.parametrize("use_caller_ws", [False, True])
+def test_graph_capture_of_the_decode_step_replays_exactly(cuda, use_caller_ws):
+    """store_kvcache + paged_attention_decode recorded into a HIP graph; every replay matches eager."""
+    import torch
+    import paged_attention_decode_amd as pa
+    x = make_inputs(custom_config(dtype="bf16", batch=6, hq=16, hkv=4, lens=(1, 40, 300, 17, 1000, 64), seed=11))
+    c = x.cfg
+    dev = to_device(x, cuda)
+    ws = None
+    if use_caller_ws:
+        need = pa.workspace_bytes(c.batch, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
+                                  c.max_blocks_per_seq, pa.DTYPE_BF16, 0)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=cuda)
+    out = torch.empty((c.batch, c.num_heads, c.head_dim), dtype=torch.float32, device=cuda)
+
+    def step():
+        pa.store_kvcache(dev["k_new"], dev["v_new"], dev["slot_mapping"], dev["k_cache"], dev["v_cache"])
+        pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                  dev["context_lens"], x.scale, out, workspace=ws)
+
+    step()  # eager: allocates the library workspace if needed (allocation is not capturable)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    _, _, ref = oracle_after_store(x)
+    for rep in range(4):
+        out.fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes() == eager.cpu().numpy().tobytes(), f"replay {rep}"
+    assert np.abs(eager.cpu().numpy() - ref).max() <= 2e-3
+    # new inputs in the same buffers are picked up by a replay
+    dev["q"].copy_(dev["q"].flip(0))
+    g.replay()
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    eager2 = out.clone()
+    g.replay()
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tobytes() == eager2.cpu().numpy().tobytes()
