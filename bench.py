@@ -52,6 +52,8 @@ def parse():
                     help="leading tokens per context read with cached loads (0 library default, -1 none)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph instead of eager launches")
+    ap.add_argument("--comparators", action="store_true",
+                    help="also time a PyTorch gather-and-mask decode on the same inputs (benchmark only)")
     ap.add_argument("--cold-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="target seconds of oracle work")
@@ -163,6 +165,33 @@ def summarize_trace(workload: str, directory: str, command: str) -> Path:
     PROFILES.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")
     return path
+
+
+def torch_gather_mask_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_len):
+    """Comparator: batched gather through the block tables, masked softmax, in PyTorch (fp32 math).
+
+    The vectorised baseline of the decode benchmark the pages describe (hysenlabs MinivLLM
+    review, end of the prefilling-baseline section): gather every sequence's blocks into a
+    padded tensor, mask positions past the context, softmax, weighted sum. Used only to time
+    it beside the library; never part of the product path.
+    """
+    import torch
+    b, hq, d = q.shape
+    nb, hkv, _, bs, x = k_cache.shape
+    g = hq // hkv
+    mb = -(-max_len // bs)
+    tables = block_tables[:, :mb].long()
+    # logical [B, Hkv, T, D] views of the gathered pages
+    k = k_cache[tables]                                   # [B, MB, Hkv, D/x, bs, x]
+    k = k.permute(0, 2, 1, 4, 3, 5).reshape(b, hkv, mb * bs, d).float()
+    v = v_cache[tables]                                   # [B, MB, Hkv, bs/4, D, 4]
+    v = v.permute(0, 2, 1, 3, 5, 4).reshape(b, hkv, mb * bs, d).float()
+    qf = q.float().reshape(b, hkv, g, d)
+    scores = torch.matmul(qf, k.transpose(-1, -2).contiguous()) * scale      # [B, Hkv, G, T]
+    pos = torch.arange(mb * bs, device=q.device)
+    scores = scores.masked_fill(pos[None, None, None, :] >= context_lens[:, None, None, None], float("-inf"))
+    w = torch.softmax(scores, dim=-1)
+    return torch.matmul(w, v).reshape(b, hq, d)
 
 
 def describe(cfg) -> dict:
@@ -326,6 +355,26 @@ def main():
             cold.append(ev[0].elapsed_time(ev[1]))
         del scratch
 
+    comparators = None
+    if args.comparators:
+        print("[bench] comparator: torch gather-and-mask", file=sys.stderr, flush=True)
+        max_len = int(context_lens.max().item())
+        ref = torch_gather_mask_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, max_len)
+        torch.cuda.synchronize()
+        reps = 3
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            torch_gather_mask_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, max_len)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / reps
+        comparators = {"torch_gather_mask": {
+            "ms_per_decode": round(ms, 4), "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+            "speedup_of_library_kernel": round(ms / mean_kernel_ms, 2),
+            "max_abs_diff_vs_library": float((ref - out).abs().max().item()),
+            "note": "decode only (no store), fp32 math, padded to the longest context"}}
+        del ref
+        torch.cuda.empty_cache()
+
     traffic = traffic_from_profiles(cfg.name, kv_bytes)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -342,6 +391,8 @@ def main():
                      "kernel_mean_ms": round(mean_kernel_ms, 5),
                      "cold_kernel_median_ms": round(sorted(cold)[len(cold) // 2], 5) if cold else None},
     }
+    if comparators:
+        result["comparators"] = comparators
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(x, out.cpu().numpy(), args.cpu_budget_s)

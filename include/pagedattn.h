@@ -72,7 +72,8 @@ typedef enum pa_status {
   PA_ERR_SHAPE = 3,       /* a size is negative/zero where it must be positive, or sizes disagree */
   PA_ERR_UNSUPPORTED = 4, /* valid request outside what the kernels implement (e.g. head_dim 96) */
   PA_ERR_WORKSPACE = 5,   /* caller-provided workspace too small or misaligned */
-  PA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
+  PA_ERR_CAPACITY = 7     /* not enough free KV blocks (block manager) */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -222,6 +223,76 @@ int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, in
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                  int32_t dtype, int32_t partition_size);
+
+/*
+ * pa_copy_blocks - copy whole KV blocks (both caches, all kv heads): for each
+ * i < num_pairs, block dst[i] becomes a bit copy of block src[i]. Used for the
+ * block manager's copy-on-write. src/dst are DEVICE int32 arrays; pairs with an
+ * id outside [0, num_blocks) are skipped; a dst equal to another pair's src or
+ * dst races. Layout and dtype as for pa_store_kvcache.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int32_t dtype, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Block manager (host memory only, no device work): the allocator that turns
+ * sequences of token ids into block tables and slot mappings, with prefix
+ * caching. Passage: miniVLLM docs, "What is miniVLLM?" (paged KV cache with
+ * prefix caching); hysenlabs MinivLLM review, "The structure block ..." (block
+ * management for the KV cache) and its dependency list (token hashing).
+ *
+ * Full blocks are keyed by a chained 64-bit hash of all tokens up to and
+ * including them; a new sequence reuses every leading full block whose key and
+ * token ids match a cached block (reference counted). Freed full blocks stay
+ * cached until evicted (least recently freed first) when free blocks run out.
+ * Block ids are in [0, num_blocks); slot = block * block_size + offset.
+ * All functions are thread-safe per manager; errors return a pa_status with a
+ * message from pa_bm_last_error().
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* New manager over num_blocks blocks of block_size tokens; NULL on bad sizes. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* m);
+
+/* Registers a sequence with its prompt tokens and allocates its blocks. On
+ * success *num_cached_tokens (if non-NULL) is the number of leading tokens whose
+ * blocks were already cached (their K/V need not be recomputed or stored).
+ * PA_ERR_CAPACITY if the blocks do not fit (nothing is changed then). */
+int pa_bm_add_sequence(pa_block_manager* m, int64_t seq_id, const int32_t* tokens, int32_t num_tokens,
+                       int32_t* num_cached_tokens);
+
+/* Reserves the slot of one new token of a sequence (a decode step). If the
+ * sequence's last block was shared and partially filled, a fresh block replaces
+ * it and *copy_src / *copy_dst name the block copy the caller must perform on
+ * the device before storing the token (both -1 otherwise). */
+int pa_bm_append_token(pa_block_manager* m, int64_t seq_id, int32_t token, int32_t* slot, int32_t* copy_src,
+                       int32_t* copy_dst);
+
+/* New sequence child_id sharing all blocks of parent_id (parallel sampling). */
+int pa_bm_fork(pa_block_manager* m, int64_t parent_id, int64_t child_id);
+
+/* Releases a sequence's blocks. */
+int pa_bm_free_sequence(pa_block_manager* m, int64_t seq_id);
+
+/* Copies the sequence's block ids into out[0 .. n) (n <= max_blocks) and
+ * reports n and the token count; out may be NULL to query sizes only. */
+int pa_bm_block_table(pa_block_manager* m, int64_t seq_id, int32_t* out, int32_t max_blocks, int32_t* num_blocks,
+                      int32_t* num_tokens);
+
+/* Slots of tokens [first_token, first_token + count) of a sequence. */
+int pa_bm_slots(pa_block_manager* m, int64_t seq_id, int32_t first_token, int32_t count, int32_t* slots);
+
+/* Free-or-evictable blocks, cached (hashed) blocks, and hit/miss/eviction counters. */
+int pa_bm_stats(pa_block_manager* m, int32_t* free_blocks, int32_t* cached_blocks, int64_t* hits, int64_t* misses,
+                int64_t* evictions);
+
+/* Reference count of a block (-1 for a bad id). */
+int32_t pa_bm_block_ref(pa_block_manager* m, int32_t block);
+
+/* Message of the last failed block-manager call on this thread ("" if none). */
+const char* pa_bm_last_error(void);
 
 /* Message of the last failed call on this thread ("" if none). Never NULL. */
 const char* pa_last_error(void);

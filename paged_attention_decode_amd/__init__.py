@@ -28,7 +28,7 @@ from typing import Optional, Tuple
 __all__ = [
     "PagedAttnError", "store_kvcache", "paged_attention_decode", "allocate_kv_cache",
     "k_cache_shape", "v_cache_shape", "decode_plan", "workspace_bytes", "version", "shutdown",
-    "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16",
+    "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "BlockManager", "copy_blocks",
 ]
 
 # PAGEDATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
@@ -37,7 +37,7 @@ _lib = None
 
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_UNSUPPORTED",
-           5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+           5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY"}
 
 
 class PagedAttnError(RuntimeError):
@@ -89,6 +89,26 @@ def load_library():
     lib.pa_version.restype = ctypes.c_char_p
     lib.pa_shutdown.argtypes = []
     lib.pa_shutdown.restype = c_int
+    lib.pa_copy_blocks.argtypes = [c_p, c_p, c_p, c_p, c_int, c_int, c_int, c_int, c_i64, c_int, c_p]
+    lib.pa_copy_blocks.restype = c_int
+    p_i32, p_i64 = ctypes.POINTER(c_int), ctypes.POINTER(c_i64)
+    lib.pa_bm_create.argtypes = [c_int, c_int]
+    lib.pa_bm_create.restype = c_p
+    lib.pa_bm_destroy.argtypes = [c_p]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_add_sequence.argtypes = [c_p, c_i64, p_i32, c_int, p_i32]
+    lib.pa_bm_append_token.argtypes = [c_p, c_i64, c_int, p_i32, p_i32, p_i32]
+    lib.pa_bm_fork.argtypes = [c_p, c_i64, c_i64]
+    lib.pa_bm_free_sequence.argtypes = [c_p, c_i64]
+    lib.pa_bm_block_table.argtypes = [c_p, c_i64, p_i32, c_int, p_i32, p_i32]
+    lib.pa_bm_slots.argtypes = [c_p, c_i64, c_int, c_int, p_i32]
+    lib.pa_bm_stats.argtypes = [c_p, p_i32, p_i32, p_i64, p_i64, p_i64]
+    lib.pa_bm_block_ref.argtypes = [c_p, c_int]
+    lib.pa_bm_last_error.argtypes = []
+    lib.pa_bm_last_error.restype = ctypes.c_char_p
+    for f in (lib.pa_bm_add_sequence, lib.pa_bm_append_token, lib.pa_bm_fork, lib.pa_bm_free_sequence,
+              lib.pa_bm_block_table, lib.pa_bm_slots, lib.pa_bm_stats, lib.pa_bm_block_ref):
+        f.restype = c_int
     _lib = lib
     return lib
 
@@ -255,3 +275,90 @@ def version() -> str:
 
 def shutdown() -> None:
     _check(load_library().pa_shutdown())
+
+
+def copy_blocks(k_cache, v_cache, src, dst) -> None:
+    """Bit-copy whole blocks src[i] -> dst[i] in both caches (copy-on-write); src/dst int32 CUDA tensors."""
+    import torch
+    lib = load_library()
+    _require_cuda(k_cache, v_cache, src, dst)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D int32 tensors of one length")
+    _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src.contiguous().data_ptr(),
+                              dst.contiguous().data_ptr(), src.shape[0], hkv, d, bs, nb,
+                              _dtype_code(k_cache.dtype), _stream_of(k_cache)))
+
+
+class BlockManager:
+    """Prefix-caching KV block allocator (host C++; see pa_bm_* in pagedattn.h)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = load_library()
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self._m = self._lib.pa_bm_create(num_blocks, block_size)
+        if not self._m:
+            raise PagedAttnError(3, self._lib.pa_bm_last_error().decode())
+
+    def _check(self, rc):
+        if rc != 0:
+            raise PagedAttnError(rc, self._lib.pa_bm_last_error().decode())
+
+    def close(self):
+        if self._m:
+            self._lib.pa_bm_destroy(self._m)
+            self._m = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq_id: int, tokens) -> int:
+        """Allocate a prompt's blocks; returns the number of leading tokens already cached."""
+        arr = (ctypes.c_int32 * max(1, len(tokens)))(*[int(t) for t in tokens])
+        cached = ctypes.c_int32()
+        self._check(self._lib.pa_bm_add_sequence(self._m, seq_id, arr, len(tokens), ctypes.byref(cached)))
+        return cached.value
+
+    def append_token(self, seq_id: int, token: int):
+        """Slot for one new token, and the (src, dst) block copy to do first (or None)."""
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._check(self._lib.pa_bm_append_token(self._m, seq_id, int(token), ctypes.byref(slot),
+                                                 ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, ((src.value, dst.value) if src.value >= 0 else None)
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        self._check(self._lib.pa_bm_fork(self._m, parent_id, child_id))
+
+    def free_sequence(self, seq_id: int) -> None:
+        self._check(self._lib.pa_bm_free_sequence(self._m, seq_id))
+
+    def block_table(self, seq_id: int):
+        n, t = ctypes.c_int32(), ctypes.c_int32()
+        self._check(self._lib.pa_bm_block_table(self._m, seq_id, None, 0, ctypes.byref(n), ctypes.byref(t)))
+        out = (ctypes.c_int32 * max(1, n.value))()
+        self._check(self._lib.pa_bm_block_table(self._m, seq_id, out, n.value, None, None))
+        return list(out[:n.value])
+
+    def num_tokens(self, seq_id: int) -> int:
+        n, t = ctypes.c_int32(), ctypes.c_int32()
+        self._check(self._lib.pa_bm_block_table(self._m, seq_id, None, 0, ctypes.byref(n), ctypes.byref(t)))
+        return t.value
+
+    def slots(self, seq_id: int, first_token: int, count: int):
+        out = (ctypes.c_int32 * max(1, count))()
+        self._check(self._lib.pa_bm_slots(self._m, seq_id, first_token, count, out))
+        return list(out[:count])
+
+    def stats(self) -> dict:
+        f, c = ctypes.c_int32(), ctypes.c_int32()
+        h, m, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        self._check(self._lib.pa_bm_stats(self._m, ctypes.byref(f), ctypes.byref(c), ctypes.byref(h),
+                                          ctypes.byref(m), ctypes.byref(e)))
+        return {"free_blocks": f.value, "cached_blocks": c.value, "hits": h.value, "misses": m.value,
+                "evictions": e.value}
+
+    def block_ref(self, block: int) -> int:
+        return self._lib.pa_bm_block_ref(self._m, block)

@@ -202,6 +202,25 @@ int pa_store_kvcache(const void* k, const void* v, const int32_t* slot_mapping, 
   return ok();
 }
 
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                   void* stream) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_DTYPE, "dtype %d is not one of PA_DTYPE_F32/F16/BF16", dtype);
+  if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %d < 0", num_pairs);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE, "num_kv_heads, head_dim, block_size and num_blocks must be positive");
+  const int e = elem_bytes(dtype);
+  const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * e;
+  if (block_bytes % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !src || !dst) return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(PA_ERR_UNSUPPORTED, "caches must be 16-byte aligned");
+  hipError_t err = launch_copy_blocks(k_cache, v_cache, src, dst, num_pairs, block_bytes, num_blocks,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "copy_blocks launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
 int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                    int32_t max_blocks_per_seq, int32_t dtype, int32_t partition_size, int32_t num_cus,
                    int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce, size_t* workspace_bytes) {

@@ -74,6 +74,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid,
                          hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                              int32_t num_pairs, int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
 // Resident workgroups of the attention kernel per compute unit for this LDS size.
 hipError_t decode_groups_per_cu(int dtype, int head_dim, size_t lds_bytes, int* groups);
 

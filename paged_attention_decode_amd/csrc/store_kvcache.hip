@@ -56,7 +56,36 @@ __global__ __launch_bounds__(256) void store_kernel(const StoreArgs a) {
   }
 }
 
+// Whole-block copies for copy-on-write: one thread per (pair, 16-byte chunk of a block's
+// K or V region); a block is num_kv_heads contiguous pages in each cache.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* k_cache, char* v_cache, const int32_t* src,
+                                                          const int32_t* dst, int32_t num_pairs, int64_t block_bytes,
+                                                          int64_t num_blocks) {
+  const int64_t chunks = block_bytes / 16;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)num_pairs * chunks * 2) return;
+  const int64_t pair = idx / (chunks * 2);
+  const int64_t rem = idx - pair * chunks * 2;
+  const bool is_v = rem >= chunks;
+  const int64_t c = is_v ? rem - chunks : rem;
+  const int64_t s = src[pair], d = dst[pair];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  char* base = is_v ? v_cache : k_cache;
+  const u4 v = *reinterpret_cast<const u4*>(base + s * block_bytes + c * 16);
+  *reinterpret_cast<u4*>(base + d * block_bytes + c * 16) = v;
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                              int32_t num_pairs, int64_t block_bytes, int64_t num_blocks, hipStream_t st) {
+  const int64_t threads = (int64_t)num_pairs * (block_bytes / 16) * 2;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), src, dst, num_pairs,
+                     block_bytes, num_blocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t st) {
   const int e = elem_bytes(dtype);
