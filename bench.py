@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0, help="0 balanced split, -1 one pass, >0 fixed")
     ap.add_argument("--cached-prefix-tokens", type=int, default=0,
                     help="leading tokens per context read with cached loads (0 library default, -1 none)")
+    ap.add_argument("--fused-step", action="store_true",
+                    help="run each step as one pa_decode_step launch (scatter fused into the attention kernel)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph instead of eager launches")
     ap.add_argument("--comparators", action="store_true",
@@ -283,6 +285,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
+        if args.fused_step:
+            pa.decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, x.scale, out,
+                           partition_size=args.partition_size, cached_prefix_tokens=args.cached_prefix_tokens,
+                           events=events)
+            return
         pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache)
         pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
                                   partition_size=args.partition_size,
@@ -382,7 +389,9 @@ def main():
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the workload)",
         "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
                        partition_size=args.partition_size, cached_prefix_tokens=args.cached_prefix_tokens,
-                       launch="hip graph replay" if args.graph else "eager", parallelism="single GPU"),
+                       launch="hip graph replay" if args.graph else "eager",
+                       step="pa_decode_step (fused scatter + attention)" if args.fused_step
+                       else "pa_store_kvcache + pa_paged_attention_decode", parallelism="single GPU"),
         "tokens_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

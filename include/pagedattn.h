@@ -206,6 +206,33 @@ int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void*
                                  const pa_decode_opts* opts, void* stream);
 
 /*
+ * pa_decode_step - the decode step's scatter and attention in one launch.
+ *
+ * Same result as pa_store_kvcache of each sequence's new token followed by
+ * pa_paged_attention_decode_ex: for every sequence s with L_s = context_lens[s]
+ * >= 1, the token at position L_s - 1 (offset (L_s-1) % block_size of block
+ * block_tables[s][(L_s-1) / block_size]) gets k_new[s] / v_new[s] in the
+ * caches (bit copies), and the attention over tokens 0 .. L_s-1 uses them.
+ * The wavefront that computes the tile holding that token takes the new K/V
+ * from k_new/v_new directly and writes them to the cache slot, so no separate
+ * scatter kernel runs. Passage: as for the two entry points it fuses (the
+ * decode step of the paged engine, miniVLLM docs, "What is miniVLLM?").
+ *
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim] of `dtype`, inner dims
+ *                 contiguous, sequences k_new_stride / v_new_stride ELEMENTS
+ *                 apart; 16-byte aligned rows.
+ *   Other arguments as for pa_paged_attention_decode_ex (k_cache/v_cache are
+ *   written). Each new token's slot must not hold another token of the same
+ *   step (slot uniqueness, as for pa_store_kvcache).
+ */
+int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride, int64_t v_new_stride,
+                   void* k_cache, void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                   float scale, void* out, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                   int64_t q_seq_stride, int32_t dtype, int32_t out_dtype, const pa_decode_opts* opts,
+                   void* stream);
+
+/*
  * Launch plan of a decode call: pure host arithmetic, no device access when
  * num_cus > 0 (num_cus <= 0 queries the current device). Fills any non-NULL
  * output: the wavefront count of the attention kernel; range_tokens, the

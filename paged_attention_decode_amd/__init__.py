@@ -29,6 +29,7 @@ __all__ = [
     "PagedAttnError", "store_kvcache", "paged_attention_decode", "allocate_kv_cache",
     "k_cache_shape", "v_cache_shape", "decode_plan", "workspace_bytes", "version", "shutdown",
     "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "BlockManager", "copy_blocks",
+    "decode_step",
 ]
 
 # PAGEDATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
@@ -78,6 +79,9 @@ def load_library():
     lib.pa_paged_attention_decode.restype = c_int
     lib.pa_paged_attention_decode_ex.argtypes = dec + [ctypes.POINTER(DecodeOpts), c_p]
     lib.pa_paged_attention_decode_ex.restype = c_int
+    lib.pa_decode_step.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_f, c_p, c_int, c_int, c_int,
+                                   c_int, c_int, c_int, c_i64, c_i64, c_int, c_int, ctypes.POINTER(DecodeOpts), c_p]
+    lib.pa_decode_step.restype = c_int
     lib.pa_decode_plan.argtypes = [c_int] * 9 + [ctypes.POINTER(c_i64), ctypes.POINTER(c_int),
                                                  ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_plan.restype = c_int
@@ -245,6 +249,57 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
         float(scale), out.data_ptr(), bsz, hq, hkv, d, bs, block_tables.shape[1], nb, q.stride(0),
         _dtype_code(q.dtype), _dtype_code(out.dtype), ctypes.byref(opts), _stream_of(q)))
+    return out
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
+                out_dtype=None, partition_size: int = 0, cached_prefix_tokens: int = 0, workspace=None,
+                events=None):
+    """Fused decode step: write k_new/v_new ([B, Hkv, D]) at position L-1 of each sequence and attend.
+
+    Same result as store_kvcache (at each sequence's last position) followed by
+    paged_attention_decode, in one kernel launch.
+    """
+    import torch
+    lib = load_library()
+    _require_cuda(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != d or q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError(f"q must be [B, Hq, {d}] with contiguous head rows")
+    bsz, hq = q.shape[0], q.shape[1]
+    for t in (k_new, v_new):
+        if t.dim() != 3 or tuple(t.shape) != (bsz, hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"k_new, v_new must be [{bsz}, {hkv}, {d}] with contiguous head rows")
+    if q.dtype != k_cache.dtype or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("q, k_new, v_new and the caches must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != bsz or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous [B, max_blocks] tensor")
+    if context_lens.shape != (bsz,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] tensor")
+    if out is None:
+        odt = out_dtype if out_dtype is not None else q.dtype
+        out = torch.empty((bsz, hq, d), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (bsz, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor")
+    opts = DecodeOpts()
+    opts.partition_size = int(partition_size)
+    opts.cached_prefix_tokens = int(cached_prefix_tokens)
+    if workspace is not None:
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    if events is not None:
+        for ev in events:
+            if not ev.cuda_event:
+                ev.record()
+        opts.event_begin = events[0].cuda_event
+        opts.event_end = events[1].cuda_event
+    _check(lib.pa_decode_step(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), v_new.stride(0), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale), out.data_ptr(), bsz, hq,
+        hkv, d, bs, block_tables.shape[1], nb, q.stride(0), _dtype_code(q.dtype), _dtype_code(out.dtype),
+        ctypes.byref(opts), _stream_of(q)))
     return out
 
 

@@ -254,12 +254,17 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
   return bytes;
 }
 
-int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
-                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-                                 int64_t q_seq_stride, int32_t dtype, int32_t out_dtype,
-                                 const pa_decode_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the decode entry points; k_new/v_new non-null = fused scatter of the step's token.
+int decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                int64_t num_blocks, int64_t q_seq_stride, int32_t dtype, int32_t out_dtype,
+                const pa_decode_opts* opts, void* stream, const void* k_new, const void* v_new,
+                int64_t k_new_stride, int64_t v_new_stride) {
   const int32_t psize = opts ? opts->partition_size : 0;
   int rc = check_decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
                               psize);
@@ -337,6 +342,10 @@ int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void*
   a.out_f32 = out_dtype == PA_DTYPE_F32 ? 1 : 0;
   a.num_waves = (int32_t)p.num_waves;
   a.range_tiles = p.range_tiles;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_new_stride = k_new_stride;
+  a.v_new_stride = v_new_stride;
   {
     const int32_t hint = opts ? opts->cached_prefix_tokens : 0;
     a.cached_prefix_tokens = hint == 0 ? PA_DEFAULT_CACHED_PREFIX_TOKENS : (hint < 0 ? 0 : hint);
@@ -358,6 +367,43 @@ int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void*
     if (err != hipSuccess) return fail(PA_ERR_HIP, "reduce launch failed: %s", hipGetErrorString(err));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int64_t q_seq_stride, int32_t dtype, int32_t out_dtype,
+                                 const pa_decode_opts* opts, void* stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_heads, num_kv_heads,
+                     head_dim, block_size, max_blocks_per_seq, num_blocks, q_seq_stride, dtype, out_dtype, opts,
+                     stream, nullptr, nullptr, 0, 0);
+}
+
+int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride, int64_t v_new_stride,
+                   void* k_cache, void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                   float scale, void* out, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                   int64_t q_seq_stride, int32_t dtype, int32_t out_dtype, const pa_decode_opts* opts,
+                   void* stream) {
+  if (num_seqs > 0) {
+    if (!k_new || !v_new) return fail(PA_ERR_NULL, "k_new and v_new are required");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (num_kv_heads > 0 && head_dim > 0 && (k_new_stride < row || v_new_stride < row))
+      return fail(PA_ERR_SHAPE, "k_new/v_new strides smaller than num_kv_heads*head_dim");
+    if (valid_dtype(dtype)) {
+      const int e = elem_bytes(dtype);
+      if (!aligned16(k_new) || !aligned16(v_new) || (k_new_stride * e) % 16 != 0 || (v_new_stride * e) % 16 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "k_new and v_new must be 16-byte aligned with 16-byte strides");
+    }
+  }
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_heads, num_kv_heads,
+                     head_dim, block_size, max_blocks_per_seq, num_blocks, q_seq_stride, dtype, out_dtype, opts,
+                     stream, k_new, v_new, k_new_stride, v_new_stride);
 }
 
 int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

@@ -115,7 +115,7 @@ __device__ __forceinline__ void store8(void* out, int64_t idx, const float (&v)[
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, bool FUSE>
 struct Piece {
   using C = Cfg<DT, D>;
 
@@ -166,6 +166,28 @@ struct Piece {
       int bt_first = INT32_MIN / 2;
       int bt_val = 0;
 
+      // Fused scatter (pa_decode_step): the step's new token sits at position L-1, in
+      // row r0 of tile tl. The wavefront computing that tile takes its K/V from
+      // k_new/v_new (patched into the loaded registers) and, for head group 0,
+      // writes them to the token's cache slot.
+      const int tl = (L - 1) >> 4;
+      const int r0 = (L - 1) & (kTile - 1);
+      const bool fuse = FUSE && tl >= lt0 && tl < lt1;
+      u4 knew[C::kLoads];           // key chunk 4j + kq (used by the lanes of row r0)
+      uint32_t vnew[C::kLoads];     // value dims 32w + 2ln, +1 (16-bit) or dim 16u + ln (fp32)
+      int64_t blk_new = 0;
+      if (fuse) {
+        // Loaded before the tile loop: older than every tile load, so they add no waits inside it.
+        const char* kn = reinterpret_cast<const char*>(a.k_new) + ((int64_t)s * a.k_new_stride + (int64_t)g * D) * C::kE;
+        const char* vn = reinterpret_cast<const char*>(a.v_new) + ((int64_t)s * a.v_new_stride + (int64_t)g * D) * C::kE;
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j) {
+          knew[j] = *reinterpret_cast<const u4*>(kn + (4 * j + kq) * 16);
+          vnew[j] = (DT == kF32) ? *reinterpret_cast<const uint32_t*>(vn + (16 * j + ln) * 4)
+                                 : *reinterpret_cast<const uint32_t*>(vn + (32 * j + 2 * ln) * 2);
+        }
+      }
+
       auto load_tile = [&](int i, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
         const int t0 = i * kTile;
         const int page = t0 >> a.bs_log2;
@@ -177,6 +199,7 @@ struct Piece {
         }
         int64_t blk = __builtin_amdgcn_readlane(bt_val, page - bt_first);
         blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
+        if (fuse && i == tl) blk_new = blk;
         // One buffer resource per page: the page's base in scalar registers,
         // 32-bit lane offsets, and loads past the page end return zero.
         const __amdgpu_buffer_rsrc_t kr = page_rsrc(kbase + blk * blk_stride, page_bytes32);
@@ -196,7 +219,43 @@ struct Piece {
         }
       };
 
-      auto compute_tile = [&](int i, const u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+      auto compute_tile = [&](int i, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+        if (fuse && i == tl) {
+          const int i0 = r0 & 3;
+          const bool krow = ln == r0, vrow = kq == (r0 >> 2);
+          const int off0 = (tl * kTile) & (bs - 1);
+          char* kdst = const_cast<char*>(kbase) + blk_new * blk_stride + (int64_t)k_lane + off0 * 16;
+          char* vdst = const_cast<char*>(vbase) + blk_new * blk_stride + (int64_t)v_lane + (int64_t)off0 * D * C::kE;
+          const bool write = hg == 0;
+#pragma unroll
+          for (int j = 0; j < C::kLoads; ++j) {
+            if (krow) {
+              kb[j] = knew[j];
+              if (write) *reinterpret_cast<u4*>(kdst + j * 64 * bs) = knew[j];
+            }
+            if (vrow) {
+              if constexpr (DT == kF32) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vb[j][c] = (c == i0) ? vnew[j] : vb[j][c];
+                if (write) *reinterpret_cast<uint32_t*>(vdst + j * 256 + i0 * 4) = vnew[j];
+              } else {
+                // dword c holds tokens 2c, 2c+1 of the even dim (c < 2) or of the odd dim (c >= 2)
+                const uint32_t lo = vnew[j] & 0xFFFFu, hi = vnew[j] >> 16;
+                const uint32_t keep = (i0 & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                const int sh = (i0 & 1) * 16;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                  const uint32_t nv = (c < 2 ? lo : hi) << sh;
+                  vb[j][c] = ((c & 1) == (i0 >> 1)) ? ((vb[j][c] & keep) | nv) : vb[j][c];
+                }
+                if (write) {
+                  *reinterpret_cast<uint16_t*>(vdst + j * 256 + i0 * 2) = (uint16_t)lo;
+                  *reinterpret_cast<uint16_t*>(vdst + j * 256 + 8 + i0 * 2) = (uint16_t)hi;
+                }
+              }
+            }
+          }
+        }
         // S[token 4kq + r][head ln] for r = 0..3
         f4 sv = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -370,7 +429,7 @@ struct Piece {
   }
 };
 
-template <int DT, int D>
+template <int DT, int D, bool FUSE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]: first global tile of each sequence
   __shared__ int32_t s_wsum[kWavesPerGroup];
@@ -388,7 +447,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       const int r = seg - s * H;
       const int L = clamp_len(a.context_lens[s], max_len);
       const int tiles = max(1, (L + kTile - 1) / kTile);
-      Piece<DT, D>::run(a, s, r, L, 0, tiles, true, wave, 0, lane);
+      Piece<DT, D, FUSE>::run(a, s, r, L, 0, tiles, true, wave, 0, lane);
     }
     return;
   }
@@ -458,7 +517,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       // This wavefront holds the segment's first piece: record where all pieces are.
       a.ws_meta[(int64_t)s * H + r] = make_int4(wave, slot, (t + tiles - 1) / R, 0);
     }
-    Piece<DT, D>::run(a, s, r, L, lt, lt + n, complete, wave, slot, lane);
+    Piece<DT, D, FUSE>::run(a, s, r, L, lt, lt + n, complete, wave, slot, lane);
     t += n;
     if (t >= t_end) break;
     first = false;
@@ -557,7 +616,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
 
 template <int DT, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<DT, D>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
+  if (a.k_new != nullptr)
+    hipLaunchKernelGGL((decode_kernel<DT, D, true>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT, D, false>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -570,7 +632,7 @@ hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
 
 template <int DT, int D>
 hipError_t occupancy_t(size_t lds, int* groups) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups, decode_kernel<DT, D>, kDecodeThreads, lds);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups, decode_kernel<DT, D, false>, kDecodeThreads, lds);
 }
 
 }  // namespace

@@ -52,6 +52,11 @@ struct DecodeArgs {
   int32_t num_waves;      // wavefronts launched
   int32_t range_tiles;    // >0 fixed tiles per wavefront, 0 balanced, -1 one pass
   int32_t cached_prefix_tokens;  // tiles starting before this token use cached loads, later ones stream
+  // Fused scatter of the step's token at position L-1 (null: plain decode).
+  const void* k_new;      // [num_seqs][num_kv_heads][head_dim]
+  const void* v_new;
+  int64_t k_new_stride;   // elements between sequences
+  int64_t v_new_stride;
 };
 
 struct StoreArgs {

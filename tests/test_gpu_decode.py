@@ -319,3 +319,40 @@ def test_graph_capture_of_the_decode_step_replays_exactly(cuda, use_caller_ws):
     g.replay()
     torch.cuda.synchronize()
     assert out.cpu().numpy().tobytes() == eager2.cpu().numpy().tobytes()
+
+
+def _fused_vs_two_calls(cuda, x, psize, out_dtype=None):
+    import torch
+    import paged_attention_decode_amd as pa
+    odt = out_dtype or torch.float32
+    dev_a = to_device(x, cuda)
+    out_a = _run_step(dev_a, x, partition_size=psize, out_dtype=odt)
+    dev_b = to_device(x, cuda)
+    out_b = pa.decode_step(dev_b["q"], dev_b["k_new"], dev_b["v_new"], dev_b["k_cache"], dev_b["v_cache"],
+                           dev_b["block_tables"], dev_b["context_lens"], x.scale, out_dtype=odt,
+                           partition_size=psize)
+    torch.cuda.synchronize()
+    dt = x.cfg.dtype
+    assert torch_to_np(dev_b["k_cache"], dt).tobytes() == torch_to_np(dev_a["k_cache"], dt).tobytes()
+    assert torch_to_np(dev_b["v_cache"], dt).tobytes() == torch_to_np(dev_a["v_cache"], dt).tobytes()
+    assert out_b.cpu().numpy().tobytes() == out_a.cpu().numpy().tobytes()
+    return out_b
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("psize", [-1, 0, 16])
+def test_fused_step_equals_store_then_decode(cuda, case, psize):
+    dt, b, hq, hkv, d, bs, lens = CASES[case]
+    _say(f"[gpu] fused step {CASES[case]} partition_size={psize}")
+    x = make_inputs(custom_config(dtype=dt, batch=b, hq=hq, hkv=hkv, d=d, bs=bs, lens=lens, seed=200 + case))
+    x.slot_mapping[x.context_lens == 0] = -1   # no token to store for an empty context
+    out = _fused_vs_two_calls(cuda, x, psize).cpu().numpy()
+    _, _, ref = oracle_after_store(x)
+    assert np.abs(out - ref).max() <= TOL[dt]
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_bf16", "llama32_1b_fp16", "skewed_prefix_bf16"])
+def test_fused_step_full_configs(cuda, name):
+    _say(f"[gpu] fused step full config {name}")
+    x = _inputs(name)
+    _fused_vs_two_calls(cuda, x, 0)
