@@ -16,7 +16,9 @@ closed forms (one token returns its value row, equal keys return the mean of
 V, hand-derived weights in ``tests/golden/``); invariants (weights sum to one,
 relabelling physical blocks changes nothing, key shift, affine values, the
 grouped-query head mapping); the split/merge identity against the dense
-result; and the cache layout against numpy reshape/transpose construction.
+result; the cache layout against numpy reshape/transpose construction; and
+the causal prefill against SDPA with a causal or offset mask and against the
+decode definition for one new token.
 No oracle function is left unpinned.
 """
 
@@ -28,6 +30,7 @@ from .paged_attention import (  # noqa: F401
     gather_kv,
     k_index,
     merge_partitions,
+    prefill,
     store_kvcache,
     v_index,
     widen,

@@ -243,3 +243,39 @@ def decode_split(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_
             out[s, h] = merge_partitions(lse[h], parts[h])
         all_lse[s], all_parts[s] = lse, parts
     return out, all_lse, all_parts
+
+
+def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_tables: np.ndarray,
+            context_lens: np.ndarray, query_start: np.ndarray, scale: float, geo: CacheGeometry,
+            seqs: Optional[List[int]] = None) -> np.ndarray:
+    """Causal attention of each sequence's new tokens over its paged context; float64 ``[T, Hq, D]``.
+
+    Sequence s owns query rows query_start[s] .. query_start[s+1]-1 of q
+    (``[T, Hq, D]`` storage form). With n_s of them and L_s = context_lens[s]
+    tokens in the cache (the new ones included), query i sits at position
+    p = L_s - n_s + i and attends to tokens 0 .. p (flash-attention prefill of
+    the miniVLLM docs, "What is miniVLLM?"; the standard materialised form of
+    the hysenlabs MinivLLM review, prefilling-baseline section). n_s = 1 is
+    the decode case.
+    """
+    t_total, hq, dim = q.shape
+    qf = widen(q, geo.dtype)
+    group = hq // geo.num_kv_heads
+    sigma = _scale64(scale)
+    out = np.zeros((t_total, hq, dim), dtype=np.float64)
+    rows = range(len(context_lens)) if seqs is None else seqs
+    for s in rows:
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        n, length = q1 - q0, int(context_lens[s])
+        if n == 0:
+            continue
+        assert n <= length, "more new tokens than context"
+        k, v = gather_kv(k_cache, v_cache, block_tables[s], length, geo)
+        for i in range(n):
+            p = length - n + i
+            for h in range(hq):
+                g = h // group
+                z = sigma * (k[:p + 1, g, :] @ qf[q0 + i, h])
+                e = np.exp(z - z.max())
+                out[q0 + i, h] = (e / e.sum()) @ v[:p + 1, g, :]
+    return out

@@ -350,3 +350,59 @@ def test_pins_catch_planted_mistakes(monkeypatch, mutant):
         except AssertionError:
             failed += 1
     assert failed >= 1, f"no pin caught the planted {mutant} mistake"
+
+
+# ---------------------------------------------------------------- causal prefill
+
+def _sdpa_causal(q64, k64, v64, scale, offset):
+    """SDPA (float64) with query i allowed keys 0 .. offset + i."""
+    import torch
+    n, hq, d = q64.shape
+    L, hkv, _ = k64.shape
+    g = hq // hkv
+    qt = torch.from_numpy(q64).permute(1, 0, 2).reshape(1, hq, n, d)
+    kt = torch.from_numpy(k64).permute(1, 0, 2).repeat_interleave(g, dim=0).reshape(1, hq, L, d).contiguous()
+    vt = torch.from_numpy(v64).permute(1, 0, 2).repeat_interleave(g, dim=0).reshape(1, hq, L, d).contiguous()
+    allowed = torch.arange(L)[None, :] <= (offset + torch.arange(n))[:, None]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed, scale=scale)
+    return out.reshape(hq, n, d).permute(1, 0, 2).numpy()
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(seed=st.integers(0, 2**31 - 1), g=st.sampled_from([1, 2, 4]), hkv=st.sampled_from([1, 2]),
+       dtype=st.sampled_from(["fp32", "bf16", "fp16"]), data=st.data())
+def test_prefill_matches_sdpa_with_causal_offset_mask(seed, g, hkv, dtype, data):
+    lens = data.draw(st.lists(st.integers(1, 40), min_size=1, max_size=3))
+    news = [data.draw(st.integers(1, L)) for L in lens]
+    rng = np.random.default_rng(seed)
+    d = 16
+    case = PagedCase(rng, len(lens), g * hkv, hkv, d, 8, lens, dtype=dtype)
+    from workloads import to_storage
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = to_storage(rng.standard_normal((int(qs[-1]), g * hkv, d), dtype=np.float32), dtype)
+    out = oracle.prefill(q, case.k_cache, case.v_cache, case.tables, case.lens, qs, 0.3, case.geometry())
+    for s, (L, n) in enumerate(zip(lens, news)):
+        ref = _sdpa_causal(widen_np(q[qs[s]:qs[s + 1]], dtype), widen_np(case.k_dense[s], dtype),
+                           widen_np(case.v_dense[s], dtype), _scale32(0.3), L - n)
+        np.testing.assert_allclose(out[qs[s]:qs[s + 1]], ref, atol=1e-12)
+
+
+def test_prefill_of_one_new_token_is_decode():
+    rng = np.random.default_rng(21)
+    case = PagedCase(rng, 3, 8, 2, 32, 8, [9, 1, 30], dtype="bf16")
+    qs = np.arange(4, dtype=np.int32)
+    out = oracle.prefill(case.q, case.k_cache, case.v_cache, case.tables, case.lens, qs, 0.2, case.geometry())
+    dec = oracle.decode(case.q, case.k_cache, case.v_cache, case.tables, case.lens, 0.2, case.geometry())
+    np.testing.assert_array_equal(out, dec)
+
+
+def test_prefill_first_token_returns_its_value_row():
+    # query 0 of a full prefill (n == L) sees only token 0
+    rng = np.random.default_rng(22)
+    case = PagedCase(rng, 1, 4, 2, 16, 4, [12], dtype="fp32")
+    from workloads import to_storage
+    q = to_storage(rng.standard_normal((12, 4, 16), dtype=np.float32), "fp32")
+    out = oracle.prefill(q, case.k_cache, case.v_cache, case.tables, case.lens, np.array([0, 12], np.int32), 0.5,
+                         case.geometry())
+    for h in range(4):
+        np.testing.assert_array_equal(out[0, h], widen_np(case.v_dense[0][0, h // 2], "fp32"))
