@@ -52,6 +52,9 @@ def parse():
                     help="leading tokens per context read with cached loads (0 library default, -1 none)")
     ap.add_argument("--fused-step", action="store_true",
                     help="run each step as one pa_decode_step launch (scatter fused into the attention kernel)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time pa_paged_prefill instead: every context token of the workload is a prompt token "
+                         "(full causal prefill); prints its own JSON line in TFLOP/s")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph instead of eager launches")
     ap.add_argument("--comparators", action="store_true",
@@ -146,7 +149,7 @@ def summarize_pmc(workload: str, fetch_dir: str, write_dir: str, commands) -> Pa
     return path
 
 
-def summarize_trace(workload: str, directory: str, command: str) -> Path:
+def summarize_trace(workload: str, directory: str, command: str, kernel: str = "decode") -> Path:
     """Per-kernel duration statistics of a rocprofv3 --kernel-trace --stats run, as text."""
     import csv
     files = sorted(Path(directory).rglob("*kernel_stats.csv"))
@@ -154,7 +157,8 @@ def summarize_trace(workload: str, directory: str, command: str) -> Path:
         raise SystemExit(f"no kernel_stats.csv under {directory}")
     lines = [f"# rocprofv3 kernel statistics, workload {workload}",
              f"# command: {command}",
-             f"# summary command: python bench.py --workload {workload} --summarize-trace {directory}",
+             f"# summary command: python bench.py --workload {workload} {'--prefill ' if kernel == 'prefill' else ''}"
+             f"--summarize-trace {directory}",
              f"kernel_source_sha256: {kernel_source_sha()}",
              f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
     for r in csv.DictReader(open(files[0])):
@@ -163,7 +167,7 @@ def summarize_trace(workload: str, directory: str, command: str) -> Path:
         lines.append(f"{name:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
                      f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
                      f"{float(r['Percentage']):>6.2f}")
-    path = PROFILES / f"decode_{workload}_kernel_trace.txt"
+    path = PROFILES / f"{kernel}_{workload}_kernel_trace.txt"
     PROFILES.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")
     return path
@@ -240,13 +244,73 @@ def cpu_baseline(x, gpu_out, budget_s: float) -> dict:
             "parity_max_abs_err_vs_gpu": err}
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+
+
+def prefill_bench(args) -> None:
+    """Full-prompt causal prefill over the workload's paged caches; useful flops = 4*D*Hq*sum(n*L - n(n-1)/2)."""
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_amd as pa
+    from workloads import get_config, make_inputs, to_storage
+
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.workload)
+    print(f"[bench] prefill: generating {cfg.name}", file=sys.stderr, flush=True)
+    x = make_inputs(cfg)
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    k_cache = up(x.k_cache).view(pa.k_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, tdt))
+    v_cache = up(x.v_cache).view(pa.v_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size))
+    lens = x.context_lens.astype(np.int64)
+    qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = up(to_storage(np.random.default_rng(7).standard_normal((int(qs[-1]), cfg.num_heads, cfg.head_dim),
+                                                                dtype=np.float32), cfg.dtype))
+    bt = torch.from_numpy(x.block_tables).to(dev)
+    cl = torch.from_numpy(x.context_lens).to(dev)
+    qst = torch.from_numpy(qs).to(dev)
+    out = torch.empty((int(qs[-1]), cfg.num_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    flops = 4.0 * cfg.head_dim * cfg.num_heads * float(np.sum(lens * lens - lens * (lens - 1) / 2))
+    for _ in range(max(1, args.warmup)):
+        pa.paged_prefill(q, k_cache, v_cache, bt, cl, qst, x.scale, out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(args.steps):
+        pa.paged_prefill(q, k_cache, v_cache, bt, cl, qst, x.scale, out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    print(json.dumps({
+        "metric": "paged prefill TFLOP/s (causal, full prompts)", "value": round(tflops, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded, shapes of the workload)",
+        "config": dict(describe(cfg), prompt_tokens=int(qs[-1]), useful_flops=flops),
+        "tokens_per_s": round(float(qs[-1]) / (ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None, "kernel": "prefill_kernel",
+                     "kernel_mean_ms": round(ms, 5)}}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         print(summarize_pmc(args.workload, args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands))
         return
     if args.summarize_trace:
-        print(summarize_trace(args.workload, args.summarize_trace, args.trace_command))
+        print(summarize_trace(args.workload, args.summarize_trace, args.trace_command,
+                              "prefill" if args.prefill else "decode"))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -264,6 +328,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pa.load_library()
+    if args.prefill:
+        prefill_bench(args)
+        return
     dev = torch.device("cuda:0")
     cfg = get_config(args.workload)
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)

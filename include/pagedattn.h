@@ -233,6 +233,33 @@ int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t 
                    void* stream);
 
 /*
+ * pa_paged_prefill - causal attention of each sequence's new tokens over its
+ * paged KV cache (flash-attention prefill with online softmax: miniVLLM docs,
+ * "What is miniVLLM?" and "Explore by topic"; the materialised standard form
+ * is in the hysenlabs MinivLLM review, prefilling-baseline section).
+ *
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1 of q; with
+ * n_s of them and L_s = context_lens[s] cached tokens (the new tokens' K/V
+ * already stored, e.g. with pa_store_kvcache), query i sits at position
+ * L_s - n_s + i and attends to tokens 0 .. L_s - n_s + i. n_s = L_s is a full
+ * prefill, n_s < L_s continues after cached tokens (prefix-cache hit, chunked
+ * prefill), n_s = 1 is a decode step. Rows of q past L_s new tokens, or of a
+ * sequence with L_s = 0, are left unwritten in out.
+ *
+ *   q            [num_tokens][num_heads][head_dim], heads and dims contiguous,
+ *                tokens q_token_stride ELEMENTS apart.
+ *   query_start  [num_seqs + 1] int32, non-decreasing, query_start[num_seqs]
+ *                <= num_tokens.
+ *   out          [num_tokens][num_heads][head_dim] contiguous, fp32 or dtype.
+ *   Other arguments and limits as for pa_paged_attention_decode.
+ */
+int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                     float scale, void* out, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int64_t num_blocks, int32_t dtype, int32_t out_dtype, void* stream);
+
+/*
  * Launch plan of a decode call: pure host arithmetic, no device access when
  * num_cus > 0 (num_cus <= 0 queries the current device). Fills any non-NULL
  * output: the wavefront count of the attention kernel; range_tokens, the

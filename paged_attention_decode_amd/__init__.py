@@ -29,7 +29,7 @@ __all__ = [
     "PagedAttnError", "store_kvcache", "paged_attention_decode", "allocate_kv_cache",
     "k_cache_shape", "v_cache_shape", "decode_plan", "workspace_bytes", "version", "shutdown",
     "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "BlockManager", "copy_blocks",
-    "decode_step",
+    "decode_step", "paged_prefill",
 ]
 
 # PAGEDATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
@@ -82,6 +82,9 @@ def load_library():
     lib.pa_decode_step.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_f, c_p, c_int, c_int, c_int,
                                    c_int, c_int, c_int, c_i64, c_i64, c_int, c_int, ctypes.POINTER(DecodeOpts), c_p]
     lib.pa_decode_step.restype = c_int
+    lib.pa_paged_prefill.argtypes = [c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_f, c_p, c_int, c_int, c_int, c_int, c_int,
+                                     c_int, c_int, c_i64, c_int, c_int, c_p]
+    lib.pa_paged_prefill.restype = c_int
     lib.pa_decode_plan.argtypes = [c_int] * 9 + [ctypes.POINTER(c_i64), ctypes.POINTER(c_int),
                                                  ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_plan.restype = c_int
@@ -300,6 +303,37 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
         v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale), out.data_ptr(), bsz, hq,
         hkv, d, bs, block_tables.shape[1], nb, q.stride(0), _dtype_code(q.dtype), _dtype_code(out.dtype),
         ctypes.byref(opts), _stream_of(q)))
+    return out
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float, out=None, *,
+                  out_dtype=None):
+    """Causal attention of each sequence's new tokens (q rows query_start[s]..query_start[s+1]-1,
+    positions L-n..L-1) over its paged cache; returns out [num_tokens, Hq, D]."""
+    import torch
+    lib = load_library()
+    _require_cuda(q, k_cache, v_cache, block_tables, context_lens, query_start)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != d or q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError(f"q must be [T, Hq, {d}] with contiguous head rows")
+    t, hq = q.shape[0], q.shape[1]
+    bsz = context_lens.shape[0]
+    if q.dtype != k_cache.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    for x, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (query_start, "query_start")):
+        if x.dtype != torch.int32 or not x.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous int32 tensor")
+    if block_tables.dim() != 2 or block_tables.shape[0] != bsz or query_start.shape != (bsz + 1,):
+        raise ValueError("block_tables [B, MB], context_lens [B] and query_start [B+1] disagree")
+    if out is None:
+        odt = out_dtype if out_dtype is not None else q.dtype
+        out = torch.empty((t, hq, d), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (t, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, Hq, D] tensor")
+    _check(lib.pa_paged_prefill(q.data_ptr(), q.stride(0), k_cache.data_ptr(), v_cache.data_ptr(),
+                                block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(),
+                                float(scale), out.data_ptr(), bsz, t, hq, hkv, d, bs, block_tables.shape[1], nb,
+                                _dtype_code(q.dtype), _dtype_code(out.dtype), _stream_of(q)))
     return out
 
 

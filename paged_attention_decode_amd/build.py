@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 BUILD = PKG / "_build"
 LIB = PKG / "libpagedattn.so"
-SOURCES = ["api.hip", "decode.hip", "store_kvcache.hip", "block_manager.cpp"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "store_kvcache.hip", "block_manager.cpp"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are kept out of the generated code.

@@ -221,6 +221,63 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32
   return ok();
 }
 
+int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                     float scale, void* out, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                     int64_t num_blocks, int32_t dtype, int32_t out_dtype, void* stream) {
+  int rc = check_decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype, 0);
+  if (rc != PA_OK) return rc;
+  if (!valid_dtype(out_dtype) || (out_dtype != PA_DTYPE_F32 && out_dtype != dtype))
+    return fail(PA_ERR_DTYPE, "out_dtype %d must be PA_DTYPE_F32 or the input dtype %d", out_dtype, dtype);
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+  if (num_blocks <= 0) return fail(PA_ERR_SHAPE, "num_blocks %lld must be positive", (long long)num_blocks);
+  if (q_token_stride < (int64_t)num_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "q_token_stride %lld smaller than num_heads*head_dim", (long long)q_token_stride);
+  if (num_seqs == 0 || num_tokens == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  const int e = elem_bytes(dtype);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (q_token_stride * e) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "q, the caches and out must be 16-byte aligned (q rows too)");
+  DeviceState* st = nullptr;
+  rc = device_state(&st);
+  if (rc != PA_OK) return rc;
+  PrefillArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.out = out;
+  a.q_token_stride = q_token_stride;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.n_hg = (a.group + kHeadsPerTile - 1) / kHeadsPerTile;
+  a.gh_max = a.group < kHeadsPerTile ? a.group : kHeadsPerTile;
+  a.block_size = block_size;
+  a.bs_log2 = ilog2(block_size);
+  a.max_blocks = max_blocks_per_seq;
+  a.out_f32 = out_dtype == PA_DTYPE_F32 ? 1 : 0;
+  const int qpi = prefill_queries_per_item(head_dim, a.gh_max);
+  const int64_t items = (int64_t)num_kv_heads * a.n_hg * (((int64_t)num_tokens + qpi - 1) / qpi + num_seqs);
+  const int64_t resident = (int64_t)st->num_cus * kGroupsPerCU * kWavesPerGroup;
+  int64_t waves = items < resident ? items : resident;
+  if (waves < 1) waves = 1;
+  const int grid = (int)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
+  a.num_waves = grid * kWavesPerGroup;
+  hipError_t err = launch_prefill(a, dtype, head_dim, grid, (size_t)(num_seqs + 1) * sizeof(int32_t),
+                                  reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
+  return ok();
+}
+
 int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                    int32_t max_blocks_per_seq, int32_t dtype, int32_t partition_size, int32_t num_cus,
                    int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce, size_t* workspace_bytes) {

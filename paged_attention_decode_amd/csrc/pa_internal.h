@@ -74,7 +74,35 @@ struct StoreArgs {
   int32_t block_size;
 };
 
+struct PrefillArgs {
+  const void* q;                // [num_tokens][num_heads][head_dim], token stride q_token_stride
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;   // [num_seqs + 1]
+  void* out;                    // [num_tokens][num_heads][head_dim]
+  int64_t q_token_stride;
+  int64_t num_blocks;
+  float scale_log2;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t n_hg;
+  int32_t gh_max;
+  int32_t block_size;
+  int32_t bs_log2;
+  int32_t max_blocks;
+  int32_t out_f32;
+  int32_t num_waves;
+};
+
 // Launchers (return the launch error, hipSuccess otherwise).
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
+                          hipStream_t stream);
+// Query tokens one prefill work item covers.
+int prefill_queries_per_item(int head_dim, int gh_max);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
                          hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);

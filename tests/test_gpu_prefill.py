@@ -1,0 +1,95 @@
+"""GPU parity of pa_paged_prefill (causal attention of new tokens over the paged cache) against the oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_inputs, to_storage
+from _gpu_helpers import TOL, custom_config, geometry, half_ulp, np_to_torch, to_device, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, Hq, Hkv, D, bs, context lengths, new tokens per sequence
+    ("bf16", 8, 2, 128, 16, (40, 17, 100), (40, 17, 100)),        # full prefills
+    ("bf16", 8, 2, 128, 16, (300, 64, 129), (37, 1, 64)),         # after cached tokens
+    ("fp16", 32, 8, 64, 16, (200, 33), (200, 5)),                 # G = 4, head_dim 64
+    ("fp32", 4, 4, 64, 32, (50, 3), (50, 3)),                     # G = 1
+    ("bf16", 16, 2, 128, 256, (520, 9), (300, 9)),                # G = 8, big blocks
+    ("bf16", 40, 2, 64, 16, (70, 31), (70, 2)),                   # G = 20: head groups 16 + 4
+    ("fp16", 6, 2, 256, 64, (90, 130), (90, 17)),                 # odd G, head_dim 256
+    ("bf16", 8, 2, 128, 16, (5, 0, 30), (5, 0, 30)),              # an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_prefill_matches_oracle(cuda, case):
+    import torch
+    import paged_attention_decode_amd as pa
+    dt, hq, hkv, d, bs, lens, news = CASES[case]
+    print(f"[gpu] prefill case {CASES[case]}", flush=True)
+    x = make_inputs(custom_config(dtype=dt, batch=len(lens), hq=hq, hkv=hkv, d=d, bs=bs, lens=lens, seed=300 + case))
+    rng = np.random.default_rng(case)
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = to_storage(rng.standard_normal((int(qs[-1]), hq, d), dtype=np.float32), dt)
+    dev = to_device(x, cuda)
+    for out_dt in ("fp32", dt):
+        out = pa.paged_prefill(np_to_torch(q, dt).to(cuda), dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                               dev["context_lens"], torch.from_numpy(qs).to(cuda), x.scale,
+                               out_dtype=torch_dtype(out_dt))
+        torch.cuda.synchronize()
+        out = out.float().cpu().numpy()
+        ref = oracle.prefill(q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, qs, x.scale, geometry(x))
+        bound = TOL[dt] + (half_ulp(ref, dt) if out_dt != "fp32" else 0.0)
+        assert (np.abs(out - ref) <= bound).all(), np.abs(out - ref).max()
+
+
+def test_prefill_of_one_token_matches_decode(cuda):
+    import torch
+    import paged_attention_decode_amd as pa
+    x = make_inputs(custom_config(dtype="bf16", batch=5, hq=16, hkv=4, lens=(1, 77, 300, 16, 1000), seed=9))
+    dev = to_device(x, cuda)
+    qs = torch.arange(6, dtype=torch.int32, device=cuda)
+    pre = pa.paged_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"], qs,
+                           x.scale, out_dtype=torch.float32)
+    dec = pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                    dev["context_lens"], x.scale, out_dtype=torch.float32, partition_size=-1)
+    torch.cuda.synchronize()
+    assert torch.allclose(pre, dec, rtol=0, atol=2e-5)
+
+
+def test_store_then_prefill_then_decode_chain(cuda):
+    """A prompt stored and prefilled, then one decode step: both against the oracle."""
+    import torch
+    import paged_attention_decode_amd as pa
+    dt, hq, hkv, d, bs = "bf16", 8, 2, 128, 16
+    prompt = 75
+    rng = np.random.default_rng(5)
+    nb = 16
+    k_cache, v_cache = pa.allocate_kv_cache(nb, hkv, d, bs, torch.bfloat16, cuda)
+    k_cache.zero_()
+    v_cache.zero_()
+    table = rng.permutation(nb)[:8].astype(np.int32)
+    kv = [to_storage(rng.standard_normal((prompt + 1, hkv, d), dtype=np.float32), dt) for _ in range(2)]
+    slots = (table[np.arange(prompt + 1) // bs] * bs + np.arange(prompt + 1) % bs).astype(np.int32)
+    pa.store_kvcache(np_to_torch(kv[0][:prompt], dt).to(cuda), np_to_torch(kv[1][:prompt], dt).to(cuda),
+                     torch.from_numpy(slots[:prompt]).to(cuda), k_cache, v_cache)
+    q = to_storage(rng.standard_normal((prompt + 1, hq, d), dtype=np.float32), dt)
+    bt = torch.from_numpy(table[None, :].copy()).to(cuda)
+    pre = pa.paged_prefill(np_to_torch(q[:prompt], dt).to(cuda), k_cache, v_cache, bt,
+                           torch.tensor([prompt], dtype=torch.int32, device=cuda),
+                           torch.tensor([0, prompt], dtype=torch.int32, device=cuda), 0.1, out_dtype=torch.float32)
+    step = pa.decode_step(np_to_torch(q[prompt:], dt).to(cuda), np_to_torch(kv[0][prompt:], dt).to(cuda),
+                          np_to_torch(kv[1][prompt:], dt).to(cuda), k_cache, v_cache, bt,
+                          torch.tensor([prompt + 1], dtype=torch.int32, device=cuda), 0.1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kd, vd = oracle.widen(kv[0], dt), oracle.widen(kv[1], dt)
+    qf = oracle.widen(q, dt)
+    for i in range(prompt + 1):
+        ref = oracle.decode_sequence(qf[i], kd[:i + 1], vd[:i + 1], 0.1)
+        got = pre[i].cpu().numpy() if i < prompt else step[0].cpu().numpy()
+        assert np.abs(got - ref).max() <= 2e-3, i
