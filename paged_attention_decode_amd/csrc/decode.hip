@@ -352,13 +352,25 @@ struct Piece {
   }
 };
 
+#ifndef PA_XCD_REMAP
+#define PA_XCD_REMAP 1
+#endif
+
 template <int DT, int D, bool FUSE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]: first global tile of each sequence
   __shared__ int32_t s_wsum[kWavesPerGroup];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+#if PA_XCD_REMAP
+  // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that consecutive
+  // ranges (neighbouring sequences, e.g. a prefix-sharing group) run on the same XCD.
+  int grp = blockIdx.x;
+  if ((gridDim.x & 7) == 0) grp = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int wave = grp * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
+#else
   const int wave = blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
+#endif
   const int max_len = a.max_blocks << a.bs_log2;
   const int H = a.segs_per_seq;
 
