@@ -23,9 +23,11 @@ LIB = PKG / "libpagedattn.so"
 SOURCES = ["api.hip", "decode.hip", "prefill.hip", "store_kvcache.hip", "block_manager.cpp"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
-# Packed fp32 instructions are kept out of the generated code.
+# Packed fp32 instructions are kept out of the generated code. Matrix-core results stay in
+# ordinary VGPRs (no accumulator-register copies around the online-softmax rescale).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", str(INCLUDE), "-I", str(CSRC)]
 
 

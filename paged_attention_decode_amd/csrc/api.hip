@@ -35,7 +35,10 @@ int ok() {
 
 // Attention-kernel workgroups per compute unit that one call plans for.
 // Ranges are sized for this many resident wavefronts (4 per workgroup).
-constexpr int kGroupsPerCU = 2;
+#ifndef PA_GROUPS_PER_CU
+#define PA_GROUPS_PER_CU 2
+#endif
+constexpr int kGroupsPerCU = PA_GROUPS_PER_CU;
 
 struct DeviceState {
   bool init = false;
