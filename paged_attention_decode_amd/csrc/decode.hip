@@ -149,7 +149,9 @@ struct Piece {
           const int off0 = (tl * kTile) & (bs - 1);
           char* kdst = const_cast<char*>(kbase) + blk_new * blk_stride + (int64_t)k_lane + off0 * 16;
           char* vdst = const_cast<char*>(vbase) + blk_new * blk_stride + (int64_t)v_lane + (int64_t)off0 * D * C::kE;
-          const bool write = hg == 0;
+          // With a merge kernel (split modes) that kernel writes the slot, so this one never
+          // waits on stores; one pass has no merge kernel and writes here.
+          const bool write = hg == 0 && a.range_tiles < 0;
 #pragma unroll
           for (int j = 0; j < C::kLoads; ++j) {
             if (krow) {
@@ -160,7 +162,7 @@ struct Piece {
               if constexpr (DT == kF32) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vb[j][c] = (c == i0) ? vnew[j] : vb[j][c];
-                if (write) *reinterpret_cast<uint32_t*>(vdst + j * 256 + i0 * 4) = vnew[j];
+                if (write) *reinterpret_cast<u4*>(vdst + j * 256) = vb[j];
               } else {
                 // dword c holds tokens 2c, 2c+1 of the even dim (c < 2) or of the odd dim (c >= 2)
                 const uint32_t lo = vnew[j] & 0xFFFFu, hi = vnew[j] >> 16;
@@ -171,10 +173,10 @@ struct Piece {
                   const uint32_t nv = (c < 2 ? lo : hi) << sh;
                   vb[j][c] = ((c & 1) == (i0 >> 1)) ? ((vb[j][c] & keep) | nv) : vb[j][c];
                 }
-                if (write) {
-                  *reinterpret_cast<uint16_t*>(vdst + j * 256 + i0 * 2) = (uint16_t)lo;
-                  *reinterpret_cast<uint16_t*>(vdst + j * 256 + 8 + i0 * 2) = (uint16_t)hi;
-                }
+                // The lane's 16 bytes are four tokens of two dims; writing them back whole stores
+                // the new token and returns the other three the bits just loaded (same block,
+                // which only this sequence writes).
+                if (write) *reinterpret_cast<u4*>(vdst + j * 256) = vb[j];
               }
             }
           }
@@ -466,6 +468,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   }
 }
 
+// Fused decode step, split modes: cache write of sequence s's new token (position L-1) for kv
+// head g, bit copies from k_new / v_new. The attention kernel already used these values from
+// registers; they must be in the cache before the next step.
+template <int DT, int D>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, int s, int g, int lane) {
+  using C = Cfg<DT, D>;
+  const int max_len = a.max_blocks << a.bs_log2;
+  const int L = clamp_len(a.context_lens[s], max_len);
+  if (L <= 0) return;
+  const int t = L - 1;
+  int64_t blk = a.block_tables[(int64_t)s * a.max_blocks + (t >> a.bs_log2)];
+  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+  const int bs = a.block_size;
+  const int o = t & (bs - 1);
+  const int64_t page_bytes = (int64_t)bs * D * C::kE;
+  const int64_t page = (blk * a.num_kv_heads + g) * page_bytes;
+  const char* kn = reinterpret_cast<const char*>(a.k_new) + ((int64_t)s * a.k_new_stride + (int64_t)g * D) * C::kE;
+  const char* vn = reinterpret_cast<const char*>(a.v_new) + ((int64_t)s * a.v_new_stride + (int64_t)g * D) * C::kE;
+  char* kc = reinterpret_cast<char*>(const_cast<void*>(a.k_cache)) + page;
+  char* vc = reinterpret_cast<char*>(const_cast<void*>(a.v_cache)) + page;
+  // K: chunk c of the row goes to ((c * bs) + o) * 16 bytes into the page.
+  for (int c = lane; c < C::kChunks; c += 64)
+    *reinterpret_cast<u4*>(kc + ((int64_t)c * bs + o) * 16) = *reinterpret_cast<const u4*>(kn + c * 16);
+  // V: dim d goes to element ((o / 4) * D + d) * 4 + o % 4 of the page.
+  for (int d = lane; d < D; d += 64) {
+    const int64_t el = ((int64_t)(o >> 2) * D + d) * 4 + (o & 3);
+    if constexpr (DT == kF32)
+      reinterpret_cast<uint32_t*>(vc)[el] = reinterpret_cast<const uint32_t*>(vn)[d];
+    else
+      reinterpret_cast<uint16_t*>(vc)[el] = reinterpret_cast<const uint16_t*>(vn)[d];
+  }
+}
+
 // Merge of the pieces of every cut segment: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),
 // M = max_p lse_p. One wavefront per (segment, head): lane p holds piece p's lse, the pieces'
 // output rows are read eight at a time so their loads are in flight together. Summation order
@@ -484,6 +519,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   const int hg = r - g * a.n_hg;
   const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
   if (n >= gh) return;
+  if (a.k_new != nullptr && n == 0 && hg == 0) store_new_token<DT, D>(a, seg / a.segs_per_seq, g, lane);
   const int4 meta = a.ws_meta[seg];
   const int wa = meta.x, slot_a = meta.y, wb = meta.z;
   if (wb <= wa) return;  // finished inside one wavefront
