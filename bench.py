@@ -74,8 +74,10 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_sha() -> str:
-    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+def kernel_source_sha(kernel: str = "decode") -> str:
+    """sha256 of the source file that holds `kernel` ("decode" or "prefill")."""
+    src = KERNEL_SOURCE.with_name(f"{kernel}.hip")
+    return hashlib.sha256(src.read_bytes()).hexdigest()
 
 
 def traffic_from_profiles(workload: str, launches_bytes: float):
@@ -159,7 +161,7 @@ def summarize_trace(workload: str, directory: str, command: str, kernel: str = "
              f"# command: {command}",
              f"# summary command: python bench.py --workload {workload} {'--prefill ' if kernel == 'prefill' else ''}"
              f"--summarize-trace {directory}",
-             f"kernel_source_sha256: {kernel_source_sha()}",
+             f"kernel_source_sha256: {kernel_source_sha(kernel)}",
              f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
     for r in csv.DictReader(open(files[0])):
         name = r["Name"].replace("(anonymous namespace)::", "")
@@ -245,6 +247,47 @@ def cpu_baseline(x, gpu_out, budget_s: float) -> dict:
 
 
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+
+
+def _pcts(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"p10_us": round(float(np.percentile(a, 10)), 2), "median_us": round(float(np.median(a)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2)}
+
+
+def extra_timings(calls: dict, reps: int, stream_bytes: int, dev) -> dict:
+    """Per-call event timings (p10 / median / p90) of each callable, measured back to back.
+
+    Also times torch's sum over `stream_bytes` of fp32 as a plain streaming-read reference rate.
+    """
+    import torch
+    out = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for b, e in evs:
+            b.record()
+            fn()
+            e.record()
+        torch.cuda.synchronize()
+        out[name] = _pcts([b.elapsed_time(e) for b, e in evs])
+    buf = torch.ones(stream_bytes // 4, dtype=torch.float32, device=dev)
+    buf.sum()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for b, e in evs:
+        b.record()
+        buf.sum()
+        e.record()
+    torch.cuda.synchronize()
+    best = min(b.elapsed_time(e) for b, e in evs)
+    out["stream_read_reference"] = {"gbs": round(stream_bytes / (best * 1e-3) / 1e9, 1),
+                                    "what": f"torch.sum over {stream_bytes >> 30} GiB fp32, best of 5"}
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def prefill_bench(args) -> None:
@@ -449,13 +492,29 @@ def main():
         del ref
         torch.cuda.empty_cache()
 
+    # Per-call distributions, outside the timed region above. The store here rewrites the same
+    # slots with the same rows, so the cache contents do not change.
+    def decode_with(psize):
+        return lambda: pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
+                                                 partition_size=psize,
+                                                 cached_prefix_tokens=args.cached_prefix_tokens)
+    calls = {"store": lambda: pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache),
+             "decode": decode_with(args.partition_size), "store_plus_decode": step}
+    for psize, name in ((0, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
+        calls[name] = decode_with(psize)
+    timings = extra_timings(calls, 20, 2 << 30, dev)
+    timings["decode_tokens_per_s"] = round(cfg.batch / (timings["decode"]["median_us"] * 1e-6), 1)
+    timings["note"] = ("cudaEvent pairs per call on the current stream, back to back (warm caches); "
+                       "decode includes the merge kernel where the plan splits")
+
     traffic = traffic_from_profiles(cfg.name, kv_bytes)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the workload)",
         "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
-                       partition_size=args.partition_size, cached_prefix_tokens=args.cached_prefix_tokens,
+                       partition_size=args.partition_size,
+                       cached_prefix_tokens=args.cached_prefix_tokens or pa.DEFAULT_CACHED_PREFIX_TOKENS,
                        launch="hip graph replay" if args.graph else "eager",
                        step="pa_decode_step (fused scatter + attention)" if args.fused_step
                        else "pa_store_kvcache + pa_paged_attention_decode", parallelism="single GPU"),
@@ -467,6 +526,7 @@ def main():
                      "kernel_mean_ms": round(mean_kernel_ms, 5),
                      "cold_kernel_median_ms": round(sorted(cold)[len(cold) // 2], 5) if cold else None},
     }
+    result["timings"] = timings
     if comparators:
         result["comparators"] = comparators
     if not args.no_cpu_baseline:

@@ -29,7 +29,7 @@ __all__ = [
     "PagedAttnError", "store_kvcache", "paged_attention_decode", "allocate_kv_cache",
     "k_cache_shape", "v_cache_shape", "decode_plan", "workspace_bytes", "version", "shutdown",
     "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "BlockManager", "copy_blocks",
-    "decode_step", "paged_prefill",
+    "decode_step", "paged_prefill", "DEFAULT_CACHED_PREFIX_TOKENS",
 ]
 
 # PAGEDATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
@@ -37,6 +37,8 @@ _LIB_PATH = Path(os.environ.get("PAGEDATTN_LIBRARY") or Path(__file__).resolve()
 _lib = None
 
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+# PA_DEFAULT_CACHED_PREFIX_TOKENS: what cached_prefix_tokens = 0 selects.
+DEFAULT_CACHED_PREFIX_TOKENS = 1024
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_UNSUPPORTED",
            5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY"}
 

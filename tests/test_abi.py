@@ -35,6 +35,14 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), f"{name} declared in pagedattn.h but not exported"
 
 
+def test_binding_constants_match_the_header():
+    text = HEADER.read_text()
+    m = re.search(r"#define\s+PA_DEFAULT_CACHED_PREFIX_TOKENS\s+(\d+)", text)
+    assert m and int(m.group(1)) == pa.DEFAULT_CACHED_PREFIX_TOKENS
+    for name, code in (("PA_DTYPE_F32", pa.DTYPE_F32), ("PA_DTYPE_F16", pa.DTYPE_F16), ("PA_DTYPE_BF16", pa.DTYPE_BF16)):
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
+
+
 def test_version(lib):
     assert pa.version().startswith("libpagedattn") and "gfx950" in pa.version()
 
