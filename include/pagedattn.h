@@ -168,7 +168,9 @@ int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_
  *   -1  one pass: every (sequence, kv head) context is handled whole by one
  *       wavefront; no reduce kernel runs.
  *   >0  fixed ranges of partition_size tokens (a multiple of 16) over the same
- *       concatenated tile stream.
+ *       concatenated tile stream. The device's resident wavefronts loop over
+ *       the ranges; the workspace has rows for the ranges of the longest
+ *       possible batch (every context max_blocks_per_seq * block_size long).
  * cached_prefix_tokens: K/V of the first cached_prefix_tokens tokens of every
  *       context are read with the default cache policy; later tokens are read
  *       with the non-temporal (streaming) policy, which moves single-use data

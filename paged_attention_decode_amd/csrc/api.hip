@@ -62,6 +62,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Plan {
   int64_t num_waves = 0;
+  int64_t num_ranges = 0;  // ranges the workspace has rows for (split modes)
   int grid = 0;
   int range_tiles = 0;  // -1 one pass, 0 balanced, >0 fixed
   bool reduce = false;
@@ -117,19 +118,25 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
     p->lds = (size_t)(num_seqs + 1) * sizeof(int32_t);
     p->reduce = true;
     if (partition_size == 0) {
+      // One range per wavefront, sized on the device from the actual lengths.
       p->range_tiles = 0;
       const int64_t useful = (upper_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave;
       waves = useful < resident ? useful : resident;
     } else {
+      // Fixed ranges: the lengths live on the device, so the workspace has rows for the
+      // ranges of the longest possible batch, and the resident wavefronts loop over the
+      // ranges the actual lengths need.
       p->range_tiles = partition_size / kTile;
-      waves = (upper_tiles + p->range_tiles - 1) / p->range_tiles;
+      p->num_ranges = (upper_tiles + p->range_tiles - 1) / p->range_tiles;
+      waves = p->num_ranges < resident ? p->num_ranges : resident;
     }
   }
   if (waves < 1) waves = 1;
   p->grid = (int)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
   p->num_waves = (int64_t)p->grid * kWavesPerGroup;
   if (p->reduce) {
-    const size_t rows = (size_t)p->num_waves * 2 * p->gh_max;
+    if (p->range_tiles == 0 || p->num_ranges < p->num_waves) p->num_ranges = p->num_waves;
+    const size_t rows = (size_t)p->num_ranges * 2 * p->gh_max;
     p->off_lse = align256(rows * head_dim * sizeof(float));
     p->off_meta = p->off_lse + align256(rows * sizeof(float));
     p->ws_bytes = p->off_meta + align256((size_t)segs * sizeof(int4));

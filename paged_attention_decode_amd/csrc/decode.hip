@@ -44,9 +44,9 @@ struct Piece {
 
   // Runs tiles [lt0, lt1) of segment (s, r). complete: the piece is the whole
   // segment, so the normalised result goes straight to `out`; otherwise to
-  // workspace slot `slot` of this wavefront.
+  // workspace slot `slot` of range `rng`.
   static __device__ __forceinline__ void run(const DecodeArgs& a, int s, int r, int L, int lt0, int lt1,
-                                             bool complete, int wave, int slot, int lane) {
+                                             bool complete, int rng, int slot, int lane) {
     const int kq = lane >> 4;  // operand k-group, and result row group
     const int ln = lane & 15;  // operand row, and result column (= head in group)
     const int g = r / a.n_hg;
@@ -327,7 +327,7 @@ struct Piece {
     if (complete) {
       base = ((int64_t)s * a.num_heads + h0 + ln) * D;
     } else {
-      const int64_t row = ((int64_t)wave * 2 + slot) * a.gh_max + ln;
+      const int64_t row = ((int64_t)rng * 2 + slot) * a.gh_max + ln;
       dst_f32 = a.ws_o;
       dst = dst_f32;
       base = row * D;
@@ -429,41 +429,46 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     const int n_eff = min(a.num_waves, max(1, (total + kMinTilesPerWave - 1) / kMinTilesPerWave));
     R = (total + n_eff - 1) / n_eff;
   }
-  int t = wave * R;
-  if (t >= total) return;
-  const int t_end = min(total, t + R);
+  // Ranges are numbered in tile order; range rho covers tiles [rho*R, rho*R + R). In the
+  // balanced mode there are at most as many ranges as wavefronts; a fixed range size can
+  // need more, and then each wavefront takes every num_waves-th range.
+  const int nranges = (total + R - 1) / R;
+  for (int rho = wave; rho < nranges; rho += a.num_waves) {
+    int t = rho * R;
+    const int t_end = min(total, t + R);
 
-  // Sequence holding tile t: largest s with s_prefix[s] <= t.
-  int lo = 0, hi = a.num_seqs;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_prefix[mid] <= t) lo = mid; else hi = mid;
-  }
-  int s = lo;
-  int L = clamp_len(a.context_lens[s], max_len);
-  int tiles = max(1, (L + kTile - 1) / kTile);
-  const int local = t - s_prefix[s];
-  int r = local / tiles;
-  int lt = local - r * tiles;
-  bool first = true;
-  while (true) {
-    const int n = min(tiles - lt, t_end - t);
-    const bool complete = (lt == 0) && (n == tiles);
-    const int slot = first ? 0 : 1;
-    if (lt == 0 && lane == 0) {
-      // This wavefront holds the segment's first piece: record where all pieces are.
-      a.ws_meta[(int64_t)s * H + r] = make_int4(wave, slot, (t + tiles - 1) / R, 0);
+    // Sequence holding tile t: largest s with s_prefix[s] <= t.
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_prefix[mid] <= t) lo = mid; else hi = mid;
     }
-    Piece<DT, D, FUSE>::run(a, s, r, L, lt, lt + n, complete, wave, slot, lane);
-    t += n;
-    if (t >= t_end) break;
-    first = false;
-    lt = 0;
-    if (++r == H) {
-      r = 0;
-      ++s;
-      L = clamp_len(a.context_lens[s], max_len);
-      tiles = max(1, (L + kTile - 1) / kTile);
+    int s = lo;
+    int L = clamp_len(a.context_lens[s], max_len);
+    int tiles = max(1, (L + kTile - 1) / kTile);
+    const int local = t - s_prefix[s];
+    int r = local / tiles;
+    int lt = local - r * tiles;
+    bool first = true;
+    while (true) {
+      const int n = min(tiles - lt, t_end - t);
+      const bool complete = (lt == 0) && (n == tiles);
+      const int slot = first ? 0 : 1;
+      if (lt == 0 && lane == 0) {
+        // This range holds the segment's first piece: record where all pieces are.
+        a.ws_meta[(int64_t)s * H + r] = make_int4(rho, slot, (t + tiles - 1) / R, 0);
+      }
+      Piece<DT, D, FUSE>::run(a, s, r, L, lt, lt + n, complete, rho, slot, lane);
+      t += n;
+      if (t >= t_end) break;
+      first = false;
+      lt = 0;
+      if (++r == H) {
+        r = 0;
+        ++s;
+        L = clamp_len(a.context_lens[s], max_len);
+        tiles = max(1, (L + kTile - 1) / kTile);
+      }
     }
   }
 }
@@ -522,9 +527,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   if (a.k_new != nullptr && n == 0 && hg == 0) store_new_token<DT, D>(a, seg / a.segs_per_seq, g, lane);
   const int4 meta = a.ws_meta[seg];
   const int wa = meta.x, slot_a = meta.y, wb = meta.z;
-  if (wb <= wa) return;  // finished inside one wavefront
+  if (wb <= wa) return;  // finished inside one range
   const int np = wb - wa + 1;
-  // Workspace row of piece p: wavefront wa + p, slot slot_a for the first piece, 0 after it.
+  // Workspace row of piece p: range wa + p, slot slot_a for the first piece, 0 after it.
   auto row_of = [&](int p) -> int64_t {
     return ((int64_t)(wa + p) * 2 + (p == 0 ? slot_a : 0)) * a.gh_max + n;
   };

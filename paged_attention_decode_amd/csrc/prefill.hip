@@ -12,8 +12,8 @@
 // streams the sequence's 16-token K/V tiles up to the block's last query and
 // keeps, per column, an online-softmax state. The 16 columns of a matrix-core
 // tile are (query, head) pairs: 16/G queries x G heads of one kv head (or 16
-// heads of one query when G > 16). Two column tiles share each K/V load when
-// head_dim <= 128. Per tile:
+// heads of one query when G > 16). Several column tiles share each K/V load:
+// four at head_dim 64, two at 128, one at 256. Per tile:
 //   S[t][c]   = K[t][:] . Q[c][:]           (rows = tokens, cols = (query, head))
 //   causal mask per column, online softmax per column
 //   O^T[d][c] += V^T[d][t] . P^T[t][c]      (P as a sum of two 16-bit parts)
@@ -28,10 +28,17 @@ namespace {
 
 using namespace dev;
 
+#ifndef PA_PREFILL_NC64
+#define PA_PREFILL_NC64 4
+#endif
+
+// Column tiles per wavefront: every K/V tile loaded serves 16 * kNC columns.
+constexpr int prefill_col_tiles(int head_dim) { return head_dim <= 64 ? PA_PREFILL_NC64 : (head_dim <= 128 ? 2 : 1); }
+
 template <int DT, int D>
 struct PrefillCfg {
   using C = Cfg<DT, D>;
-  static constexpr int kNC = (D <= 128) ? 2 : 1;  // column tiles per wavefront
+  static constexpr int kNC = prefill_col_tiles(D);
 };
 
 template <int DT, int D>
@@ -268,7 +275,11 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
   constexpr int NC = PrefillCfg<DT, D>::kNC;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that consecutive
+  // waves, which take consecutive items, run on one XCD and share its L2.
+  int grp = blockIdx.x;
+  if ((gridDim.x & 7) == 0) grp = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int wave = grp * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
   const int max_len = a.max_blocks << a.bs_log2;
   const int qb_queries = NC * (kHeadsPerTile / a.gh_max);
   const int H = a.num_kv_heads * a.n_hg;
@@ -316,10 +327,12 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
     }
     const int s = lo;
     const int local = item - s_prefix[s];
-    // Later query blocks (longer key ranges) first: they are listed first within a sequence.
+    // Within a sequence, the query blocks of one (kv head, head group) are consecutive items,
+    // so neighbouring waves stream the same K/V pages at about the same time. Later query
+    // blocks (longer key ranges) come first.
     const int nqb = (s_prefix[s + 1] - s_prefix[s]) / H;
-    const int qb = nqb - 1 - local / H;
-    const int r = local % H;
+    const int r = local / nqb;
+    const int qb = nqb - 1 - (local - r * nqb);
     prefill_item<DT, D>(a, s, r / a.n_hg, r % a.n_hg, qb, lane);
   }
 }
@@ -333,7 +346,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, int grid, size_t lds, hipStrea
 }  // namespace
 
 int prefill_queries_per_item(int head_dim, int gh_max) {
-  return (head_dim <= 128 ? 2 : 1) * (kHeadsPerTile / gh_max);
+  return prefill_col_tiles(head_dim) * (kHeadsPerTile / gh_max);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds, hipStream_t st) {

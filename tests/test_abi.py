@@ -76,6 +76,16 @@ def test_plan_fixed_ranges_cover_the_upper_bound():
     assert p["range_tokens"] == 32 and p["num_waves"] >= upper_tiles // 2
 
 
+def test_plan_fixed_ranges_loop_on_resident_waves():
+    # 2048 segments x 1024 tiles in 32-tile ranges: 65536 possible ranges, looped over by the
+    # resident wavefronts; the workspace still has two partial rows per possible range.
+    p = _plan(partition_size=512)
+    assert p["range_tokens"] == 512 and p["num_waves"] == 256 * 2 * 4
+    ranges = 256 * 8 * 1024 // 32
+    rows = ranges * 2 * 2
+    assert p["workspace_bytes"] >= rows * 128 * 4 + rows * 4 + 256 * 8 * 16
+
+
 def test_plan_small_batch_does_not_oversubscribe():
     p = _plan(num_seqs=4, num_heads=4, num_kv_heads=2, head_dim=64, max_blocks_per_seq=4, dtype_code=pa.DTYPE_F32)
     assert p["num_waves"] <= 16  # 32 tiles at most, at least 2 tiles per wavefront
