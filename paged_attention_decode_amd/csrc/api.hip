@@ -275,7 +275,7 @@ int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache,
   a.bs_log2 = ilog2(block_size);
   a.max_blocks = max_blocks_per_seq;
   a.out_f32 = out_dtype == PA_DTYPE_F32 ? 1 : 0;
-  const int qpi = prefill_queries_per_item(head_dim, a.gh_max);
+  const int qpi = prefill_queries_per_item(dtype, head_dim, a.gh_max);
   const int64_t items = (int64_t)num_kv_heads * a.n_hg * (((int64_t)num_tokens + qpi - 1) / qpi + num_seqs);
   const int64_t resident = (int64_t)st->num_cus * kGroupsPerCU * kWavesPerGroup;
   int64_t waves = items < resident ? items : resident;

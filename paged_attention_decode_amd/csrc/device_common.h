@@ -49,10 +49,29 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum over lanes l, l^16, l^32 and l^48 (the four 16-lane rows), with gfx950's row-swap
+// instructions: each swap leaves lane l's value and its partner's in the two results.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Read-only view of a table that no kernel writes while it runs (block tables): uniform reads
+// through it become scalar loads, which wait on their own counter instead of the vector one.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
 // 16-byte load at byte `off` of a buffer resource, with cache policy POL.
 template <int POL>
 __device__ __forceinline__ u4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL));
+}
+
+// 8-byte load at byte `off` of a buffer resource, with cache policy POL.
+template <int POL>
+__device__ __forceinline__ u2 buf_load8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* base, int bytes) {
@@ -82,6 +101,24 @@ __device__ __forceinline__ void store8(void* out, int64_t idx, const float (&v)[
 #pragma unroll
     for (int j = 0; j < 8; ++j) w[j] = (_Float16)v[j];
     *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(out) + idx) = w;
+  }
+}
+
+// Write 4 consecutive output values (d0 .. d0+3) of one head row.
+template <int DT>
+__device__ __forceinline__ void store4(void* out, int64_t idx, const float (&v)[4], bool out_f32) {
+  if (out_f32) {
+    *reinterpret_cast<f4*>(reinterpret_cast<float*>(out) + idx) = f4{v[0], v[1], v[2], v[3]};
+  } else if constexpr (DT == kBF16) {
+    u2 w;
+    w[0] = bf16_bits_rne(v[0]) | (bf16_bits_rne(v[1]) << 16);
+    w[1] = bf16_bits_rne(v[2]) | (bf16_bits_rne(v[3]) << 16);
+    *reinterpret_cast<u2*>(reinterpret_cast<uint16_t*>(out) + idx) = w;
+  } else if constexpr (DT == kF16) {
+    h4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (_Float16)v[j];
+    *reinterpret_cast<h4*>(reinterpret_cast<_Float16*>(out) + idx) = w;
   }
 }
 

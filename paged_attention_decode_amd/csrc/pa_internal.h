@@ -102,7 +102,7 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
                           hipStream_t stream);
 // Query tokens one prefill work item covers.
-int prefill_queries_per_item(int head_dim, int gh_max);
+int prefill_queries_per_item(int dtype, int head_dim, int gh_max);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
                          hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);

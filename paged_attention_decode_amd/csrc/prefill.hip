@@ -9,19 +9,32 @@
 // prefix-cache hit or a chunk of a chunked prefill, n = 1 a decode step.
 //
 // Work item: (sequence, kv head, head group, block of queries). One wavefront
-// streams the sequence's 16-token K/V tiles up to the block's last query and
-// keeps, per column, an online-softmax state. The 16 columns of a matrix-core
-// tile are (query, head) pairs: 16/G queries x G heads of one kv head (or 16
-// heads of one query when G > 16). Several column tiles share each K/V load:
-// four at head_dim 64, two at 128, one at 256. Per tile:
-//   S[t][c]   = K[t][:] . Q[c][:]           (rows = tokens, cols = (query, head))
-//   causal mask per column, online softmax per column
-//   O^T[d][c] += V^T[d][t] . P^T[t][c]      (P as a sum of two 16-bit parts)
-// The operand layouts are those of the decode kernel (same cache layout). K/V
-// tiles are reused by every query block of the sequence, so they are loaded
-// with the default (caching) policy.
+// streams the sequence's K/V up to the block's last query and keeps, per
+// column, an online-softmax state. The 16 columns of a matrix-core tile are
+// (query, head) pairs: 16/G queries x G heads of one kv head (or 16 heads of
+// one query when G > 16). Several column tiles share each K/V load (more at
+// smaller head_dim and 16-bit inputs, where registers allow).
+//
+// The key stream advances 32 tokens (two 16-token tiles A and B) per step:
+//   S_A, S_B = K_{A,B} . Q^T          (rows = tokens, cols = (query, head))
+//   one online-softmax update over the step's 32 keys per column
+//   O^T += V^T . P^T                  (contraction over the step's 32 keys)
+// For 16-bit inputs the second product is one 32-deep matrix-core
+// instruction per 16 output rows. Its contraction index runs over the 32 keys
+// in the order (A: 4kq..4kq+3, B: 4kq..4kq+3) for lane group kq, which is the
+// order in which the first product leaves P in registers; V^T's operand takes
+// the same order from the two tiles' V loads. P enters as a sum of two 16-bit
+// parts, value + remainder: bf16 rounded to nearest (relative error <= 2^-16),
+// fp16 rounded toward zero by the packing conversion (< 2^-20).
+//
+// K of the next step is requested as soon as this step's scores are issued,
+// V of the next step as soon as this step's second product is issued. Every
+// query block of a sequence re-reads the same keys, so the loads use the
+// default (caching) policy.
 
 #include "device_common.h"
+
+#include <float.h>
 
 namespace pa {
 namespace {
@@ -32,14 +45,20 @@ using namespace dev;
 #define PA_PREFILL_NC64 4
 #endif
 
-// Column tiles per wavefront: every K/V tile loaded serves 16 * kNC columns.
-constexpr int prefill_col_tiles(int head_dim) { return head_dim <= 64 ? PA_PREFILL_NC64 : (head_dim <= 128 ? 2 : 1); }
+// Column tiles per wavefront: every K/V load serves 16 * col_tiles columns.
+constexpr int prefill_col_tiles(int dtype, int head_dim) {
+  return dtype == kF32 ? (head_dim <= 64 ? 2 : 1)
+                       : (head_dim <= 64 ? PA_PREFILL_NC64 : (head_dim <= 128 ? 2 : 1));
+}
 
 template <int DT, int D>
 struct PrefillCfg {
   using C = Cfg<DT, D>;
-  static constexpr int kNC = prefill_col_tiles(D);
+  static constexpr int kNC = prefill_col_tiles(DT, D);
 };
+
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float fl2 __attribute__((ext_vector_type(2)));
 
 template <int DT, int D>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g, int hg, int qb, int lane) {
@@ -75,14 +94,22 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     valid[ct] = ql < qpt && hl < a.group && qi[ct] < n;
     pos[ct] = valid[ct] ? L - n + qi[ct] : p_last;
   }
+  // Logits in the log2 domain are c * (q . k) with c = |scale| * log2(e) > 0: a negative scale
+  // moves its sign into q (a sign flip, exact), and a zero scale becomes the smallest normal
+  // number, which gives the same equal weights. With c > 0 the scaling folds into exp2's
+  // argument and masked keys (-inf) stay -inf.
+  const uint32_t qflip = a.scale_log2 < 0.f ? (DT == kF32 ? 0x80000000u : 0x80008000u) : 0u;
+  const float c = fmaxf(fabsf(a.scale_log2), FLT_MIN);
   u4 qv[NC][C::kLoads];
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
     const char* qrow = reinterpret_cast<const char*>(a.q) +
                        ((int64_t)(q0 + qi[ct]) * a.q_token_stride + (int64_t)hh[ct] * D) * C::kE;
 #pragma unroll
-    for (int j = 0; j < C::kLoads; ++j)
+    for (int j = 0; j < C::kLoads; ++j) {
       qv[ct][j] = valid[ct] ? *reinterpret_cast<const u4*>(qrow + (4 * j + kq) * 16) : u4{0u, 0u, 0u, 0u};
+      qv[ct][j] ^= u4{qflip, qflip, qflip, qflip};
+    }
   }
 
   f4 acc[NC][C::kAcc];
@@ -102,149 +129,226 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * page_bytes;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
   const int64_t nb_max = a.num_blocks - 1;
+  // Lane offsets inside a page. K: chunk (4j + kq) of token (off0 + ln). V, 16-bit: 8 bytes =
+  // tokens off0 + 4kq .. +3 of dim 32w + ln (and of dim 32w + 16 + ln at +128 bytes). V, fp32:
+  // 16 bytes = tokens off0 + 4kq .. +3 of dim 16u + ln.
   const uint32_t k_lane = (uint32_t)((kq * bs + ln) * 16);
-  const uint32_t v_lane = (DT == kF32) ? (uint32_t)((kq * D + ln) * 16) : (uint32_t)((kq * D + 2 * ln) * 8);
-  int bt_first = INT32_MIN / 2;
-  int bt_val = 0;
+  const uint32_t v_lane = (DT == kF32) ? (uint32_t)((kq * D + ln) * 16) : (uint32_t)((kq * D + ln) * 8);
 
-  auto load_tile = [&](int i, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
-    const int t0 = i * kTile;
-    const int page = t0 >> a.bs_log2;
-    const int off0 = t0 & (bs - 1);
-    if (page - bt_first >= 64 || page < bt_first) {
-      bt_first = page;
-      const int idx = page + lane;
-      bt_val = idx < a.max_blocks ? bt[idx] : 0;
-    }
-    int64_t blk = __builtin_amdgcn_readlane(bt_val, page - bt_first);
-    blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
-    const __amdgpu_buffer_rsrc_t kr = page_rsrc(kbase + blk * blk_stride, page_bytes32);
-    const __amdgpu_buffer_rsrc_t vr = page_rsrc(vbase + blk * blk_stride, page_bytes32);
-    const int koff = (int)k_lane + off0 * 16;
-    const int voff = (int)v_lane + off0 * D * C::kE;
-#pragma unroll
-    for (int j = 0; j < C::kLoads; ++j) kb[j] = buf_load16<kPolicyDefault>(kr, koff + j * 64 * bs);
-#pragma unroll
-    for (int j = 0; j < C::kLoads; ++j) vb[j] = buf_load16<kPolicyDefault>(vr, voff + j * 256);
+  // Keys 0 .. p_last in 16-token tiles, two per step. Tile indices are clamped to the last
+  // tile, so every step issues the same loads: the second tile of an odd last step re-reads
+  // the first (it is masked), and the loop's final prefetch re-reads the last step. With no
+  // conditional load in the loop, the compiler's wait counts stay exact and the next step's
+  // loads overlap this step's arithmetic.
+  const int tiles = p_last / kTile + 1;
+  const int steps = (tiles + 1) >> 1;
+  auto tile_of = [&](int st, int half) { return min(2 * st + half, tiles - 1); };
+  // Block-table entries of a step's two tiles: two scalar loads, issued two steps ahead.
+  const_i32* cbt = (const_i32*)bt;
+  auto bt_load = [&](int st) -> int2 {
+    const int sc = min(st, steps - 1);
+    return make_int2(cbt[(tile_of(sc, 0) * kTile) >> a.bs_log2], cbt[(tile_of(sc, 1) * kTile) >> a.bs_log2]);
   };
-
-  auto compute_tile = [&](int i, const u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
-    const int t0 = i * kTile;
-    const bool open = t0 + kTile - 1 <= p_first;  // every key of the tile visible to every column
-    const bool past_end = t0 + kTile > L;
-    if (past_end) {
-      const bool v0 = t0 + 4 * kq + 0 < L, v1 = t0 + 4 * kq + 1 < L;
-      const bool v2 = t0 + 4 * kq + 2 < L, v3 = t0 + 4 * kq + 3 < L;
-      if constexpr (DT == kF32) {
-        const u4 msk = u4{v0 ? ~0u : 0u, v1 ? ~0u : 0u, v2 ? ~0u : 0u, v3 ? ~0u : 0u};
+  auto block = [&](int raw) -> int64_t {
+    const int64_t b = __builtin_amdgcn_readfirstlane(raw);
+    return b < 0 ? 0 : (b > nb_max ? nb_max : b);
+  };
+  u4 kA[C::kLoads], kB[C::kLoads];
+  // 16-bit: vr0[w] / vr1[w] are the second product's V^T operands for dims 32w + ln /
+  // 32w + 16 + ln, keys in P's slot order (tile A's four, then tile B's four).
+  // fp32: vr0 / vr1 are tile A's / tile B's 16-byte loads.
+  u4 vr0[C::kLoads], vr1[C::kLoads];
+  auto issue_k = [&](int st, int64_t ba, int64_t bb) {
+    const int sc = min(st, steps - 1);
+    const __amdgpu_buffer_rsrc_t ra = page_rsrc(kbase + ba * blk_stride, page_bytes32);
+    const __amdgpu_buffer_rsrc_t rb = page_rsrc(kbase + bb * blk_stride, page_bytes32);
+    const int oa = (int)k_lane + ((tile_of(sc, 0) * kTile) & (bs - 1)) * 16;
+    const int ob = (int)k_lane + ((tile_of(sc, 1) * kTile) & (bs - 1)) * 16;
 #pragma unroll
-        for (int j = 0; j < C::kLoads; ++j) vb[j] &= msk;
-      } else {
-        const uint32_t m01 = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
-        const uint32_t m23 = (v2 ? 0x0000FFFFu : 0u) | (v3 ? 0xFFFF0000u : 0u);
-        const u4 msk = u4{m01, m23, m01, m23};
+    for (int j = 0; j < C::kLoads; ++j) kA[j] = buf_load16<kPolicyDefault>(ra, oa + j * 64 * bs);
 #pragma unroll
-        for (int j = 0; j < C::kLoads; ++j) vb[j] &= msk;
+    for (int j = 0; j < C::kLoads; ++j) kB[j] = buf_load16<kPolicyDefault>(rb, ob + j * 64 * bs);
+  };
+  auto issue_v = [&](int st, int64_t ba, int64_t bb) {
+    const int sc = min(st, steps - 1);
+    const __amdgpu_buffer_rsrc_t ra = page_rsrc(vbase + ba * blk_stride, page_bytes32);
+    const __amdgpu_buffer_rsrc_t rb = page_rsrc(vbase + bb * blk_stride, page_bytes32);
+    const int oa = (int)v_lane + ((tile_of(sc, 0) * kTile) & (bs - 1)) * D * C::kE;
+    const int ob = (int)v_lane + ((tile_of(sc, 1) * kTile) & (bs - 1)) * D * C::kE;
+    if constexpr (DT == kF32) {
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) vr0[j] = buf_load16<kPolicyDefault>(ra, oa + j * 256);
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) vr1[j] = buf_load16<kPolicyDefault>(rb, ob + j * 256);
+    } else {
+#pragma unroll
+      for (int w = 0; w < C::kLoads; ++w) {
+        const u2 a0 = buf_load8<kPolicyDefault>(ra, oa + w * 256);
+        const u2 a1 = buf_load8<kPolicyDefault>(ra, oa + w * 256 + 128);
+        const u2 b0 = buf_load8<kPolicyDefault>(rb, ob + w * 256);
+        const u2 b1 = buf_load8<kPolicyDefault>(rb, ob + w * 256 + 128);
+        vr0[w] = u4{a0[0], a0[1], b0[0], b0[1]};
+        vr1[w] = u4{a1[0], a1[1], b1[0], b1[1]};
       }
     }
+  };
+  // Zero the values of keys at or beyond L (their slots may hold anything, and a zero weight
+  // times a NaN is still NaN) and of a second tile that does not exist.
+  auto mask_v = [&](int t0, bool has_b) {
+    if (t0 + 2 * kTile <= L && has_b) return;
+    uint32_t mk[2][4];
 #pragma unroll
-    for (int ct = 0; ct < NC; ++ct) {
-      f4 sv = f4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mk[h][e] = (h == 0 || has_b) && t0 + h * kTile + 4 * kq + e < L ? ~0u : 0u;
+    if constexpr (DT == kF32) {
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) {
-        if constexpr (DT == kF32) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sv = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kb[j][e]), __uint_as_float(qv[ct][j][e]), sv,
-                                                      0, 0, 0);
-        } else if constexpr (DT == kBF16) {
-          sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, kb[j]), __builtin_bit_cast(b8, qv[ct][j]),
-                                                       sv, 0, 0, 0);
-        } else {
-          sv = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kb[j]), __builtin_bit_cast(h8, qv[ct][j]),
-                                                      sv, 0, 0, 0);
-        }
+        vr0[j] &= u4{mk[0][0], mk[0][1], mk[0][2], mk[0][3]};
+        vr1[j] &= u4{mk[1][0], mk[1][1], mk[1][2], mk[1][3]};
       }
-      float z[4];
+    } else {
+      const u4 msk = u4{(mk[0][0] & 0xFFFFu) | (mk[0][1] & 0xFFFF0000u), (mk[0][2] & 0xFFFFu) | (mk[0][3] & 0xFFFF0000u),
+                        (mk[1][0] & 0xFFFFu) | (mk[1][1] & 0xFFFF0000u), (mk[1][2] & 0xFFFFu) | (mk[1][3] & 0xFFFF0000u)};
+#pragma unroll
+      for (int w = 0; w < C::kLoads; ++w) {
+        vr0[w] &= msk;
+        vr1[w] &= msk;
+      }
+    }
+  };
+  auto scores = [&](const u4 (&kb)[C::kLoads], const u4 (&q)[C::kLoads]) -> f4 {
+    f4 sv = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < C::kLoads; ++j) {
+      if constexpr (DT == kF32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sv = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kb[j][e]), __uint_as_float(q[j][e]), sv, 0, 0, 0);
+      } else if constexpr (DT == kBF16) {
+        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, kb[j]), __builtin_bit_cast(b8, q[j]), sv,
+                                                     0, 0, 0);
+      } else {
+        sv = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kb[j]), __builtin_bit_cast(h8, q[j]), sv,
+                                                    0, 0, 0);
+      }
+    }
+    return sv;
+  };
+
+  // Step -1 only issues the loads of step 0, from the same code as every later prefetch, so
+  // the compiler sees one load order and keeps its waits exact.
+  int2 bt_next = bt_load(0);
+  for (int st = -1; st < steps; ++st) {
+    const int t0 = st * 2 * kTile;
+    const bool has_b = 2 * st + 1 < tiles;
+    f4 sA[NC], sB[NC];
+    if (st >= 0) {
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        sA[ct] = scores(kA, qv[ct]);
+        sB[ct] = scores(kB, qv[ct]);
+      }
+    }
+    const int64_t nA = block(bt_next.x), nB = block(bt_next.y);
+    bt_next = bt_load(st + 2);
+    issue_k(st + 1, nA, nB);
+    // K before V in every copy of this code the compiler makes (it peels step -1).
+    __builtin_amdgcn_sched_barrier(0);
+    if (st < 0) {
+      issue_v(0, nA, nB);
+      continue;
+    }
+    mask_v(t0, has_b);
+    // every key of the step visible to every column: no masking
+    const bool open = t0 + 2 * kTile - 1 <= p_first;
+
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      float x[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        z[r] = sv[r] * a.scale_log2;
-        const int t = t0 + 4 * kq + r;
-        if (!open && (t > pos[ct] || t >= L)) z[r] = -INFINITY;
+        x[r] = sA[ct][r];
+        x[4 + r] = sB[ct][r];
       }
-      float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m[ct], mt);
+      if (!open) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = t0 + (j < 4 ? 0 : kTile) + 4 * kq + (j & 3);
+          if (t > pos[ct]) x[j] = -INFINITY;
+        }
+      }
+      float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mt = max_over_rows(mt);
+      // Key 0 is visible to every column, so m is finite from the first step on.
+      const float m_new = fmaxf(m[ct], mt * c);
       const float alpha = exp2_fast(m[ct] - m_new);
-      float p[4];
+      float p[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = exp2_fast(z[r] - m_new);
-      l[ct] = l[ct] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, -m_new));
+      l[ct] = fmaf(l[ct], alpha, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
       m[ct] = m_new;
+      // Rescale only when some column's running maximum moved in this step.
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-      for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha;
+        for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha;
+      }
+
       if constexpr (DT == kF32) {
 #pragma unroll
         for (int u = 0; u < C::kLoads; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[ct][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb[u][e]), p[e], acc[ct][u], 0, 0, 0);
-      } else if constexpr (DT == kBF16) {
-        s4 ph, pl;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t hb = bf16_bits_rne(p[r]);
-          ph[r] = (short)hb;
-          pl[r] = (short)bf16_bits_rne(p[r] - __uint_as_float(hb << 16));
-        }
-#pragma unroll
-        for (int w = 0; w < C::kLoads; ++w) {
-          const s4 a0 = __builtin_bit_cast(s4, u2{vb[w].x, vb[w].y});
-          const s4 a1 = __builtin_bit_cast(s4, u2{vb[w].z, vb[w].w});
-          acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, ph, acc[ct][2 * w], 0, 0, 0);
-          acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, pl, acc[ct][2 * w], 0, 0, 0);
-          acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, ph, acc[ct][2 * w + 1], 0, 0, 0);
-          acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, pl, acc[ct][2 * w + 1], 0, 0, 0);
-        }
+          for (int e = 0; e < 4; ++e) {
+            acc[ct][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vr0[u][e]), p[e], acc[ct][u], 0, 0, 0);
+            acc[ct][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vr1[u][e]), p[4 + e], acc[ct][u], 0, 0, 0);
+          }
       } else {
-        h4 ph, pl;
+        // P^T operand: slot j of lane group kq = key (j < 4 ? A : B) 4kq + (j & 3).
+        u4 ph, pl;
+        if constexpr (DT == kBF16) {
+          // gfx950 rounds two floats to bf16 (nearest even) in one instruction.
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const _Float16 hi = (_Float16)p[r];
-          ph[r] = hi;
-          pl[r] = (_Float16)(p[r] - (float)hi);
+          for (int i2 = 0; i2 < 4; ++i2) {
+            const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(fl2{p[2 * i2], p[2 * i2 + 1]}, bf2));
+            const float r0 = p[2 * i2] - __uint_as_float(hb << 16);
+            const float r1 = p[2 * i2 + 1] - __uint_as_float(hb & 0xFFFF0000u);
+            ph[i2] = hb;
+            pl[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(fl2{r0, r1}, bf2));
+          }
+        } else {
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            const auto hv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2], p[2 * i2 + 1]);
+            const auto lv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2] - (float)hv[0], p[2 * i2 + 1] - (float)hv[1]);
+            ph[i2] = __builtin_bit_cast(uint32_t, hv);
+            pl[i2] = __builtin_bit_cast(uint32_t, lv);
+          }
         }
 #pragma unroll
         for (int w = 0; w < C::kLoads; ++w) {
-          const h4 a0 = __builtin_bit_cast(h4, u2{vb[w].x, vb[w].y});
-          const h4 a1 = __builtin_bit_cast(h4, u2{vb[w].z, vb[w].w});
-          acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, ph, acc[ct][2 * w], 0, 0, 0);
-          acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, pl, acc[ct][2 * w], 0, 0, 0);
-          acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, ph, acc[ct][2 * w + 1], 0, 0, 0);
-          acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, pl, acc[ct][2 * w + 1], 0, 0, 0);
+          if constexpr (DT == kBF16) {
+            const b8 bh = __builtin_bit_cast(b8, ph), bl = __builtin_bit_cast(b8, pl);
+            const b8 a0 = __builtin_bit_cast(b8, vr0[w]), a1 = __builtin_bit_cast(b8, vr1[w]);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, acc[ct][2 * w + 1], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc[ct][2 * w + 1], 0, 0, 0);
+          } else {
+            const h8 hh8 = __builtin_bit_cast(h8, ph), hl8 = __builtin_bit_cast(h8, pl);
+            const h8 a0 = __builtin_bit_cast(h8, vr0[w]), a1 = __builtin_bit_cast(h8, vr1[w]);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hh8, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hl8, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hh8, acc[ct][2 * w + 1], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hl8, acc[ct][2 * w + 1], 0, 0, 0);
+          }
         }
       }
     }
-  };
-
-  // Keys 0 .. p_last; the loads of tile i+1 are in flight while tile i is computed.
-  const int tiles = p_last / kTile + 1;
-  u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads];
-  int i = 0;
-  load_tile(i, kA, vA);
-  while (true) {
-    const bool has_b = i + 1 < tiles;
-    if (has_b) load_tile(i + 1, kB, vB);
-    compute_tile(i, kA, vA);
-    if (!has_b) break;
-    const bool has_a = i + 2 < tiles;
-    if (has_a) load_tile(i + 2, kA, vA);
-    compute_tile(i + 1, kB, vB);
-    if (!has_a) break;
-    i += 2;
+    issue_v(st + 1, nA, nB);
   }
 
+  // Output rows: fp32 inputs, acc[u] row i = dim 16u + i; 16-bit inputs, acc[2w] row i =
+  // dim 32w + i and acc[2w + 1] row i = dim 32w + 16 + i. Lane (kq, ln) holds rows 4kq .. 4kq+3.
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
     float lt = l[ct] + __shfl_xor(l[ct], 16);
@@ -259,10 +363,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     } else {
 #pragma unroll
       for (int w = 0; w < C::kLoads; ++w) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = acc[ct][2 * w + (j & 1)][j >> 1] * inv;
-        store8<DT>(a.out, base + 32 * w + 8 * kq, v, a.out_f32 != 0);
+        const float v0[4] = {acc[ct][2 * w][0] * inv, acc[ct][2 * w][1] * inv, acc[ct][2 * w][2] * inv,
+                             acc[ct][2 * w][3] * inv};
+        const float v1[4] = {acc[ct][2 * w + 1][0] * inv, acc[ct][2 * w + 1][1] * inv, acc[ct][2 * w + 1][2] * inv,
+                             acc[ct][2 * w + 1][3] * inv};
+        store4<DT>(a.out, base + 32 * w + 4 * kq, v0, a.out_f32 != 0);
+        store4<DT>(a.out, base + 32 * w + 16 + 4 * kq, v1, a.out_f32 != 0);
       }
     }
   }
@@ -345,8 +451,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, int grid, size_t lds, hipStrea
 
 }  // namespace
 
-int prefill_queries_per_item(int head_dim, int gh_max) {
-  return prefill_col_tiles(head_dim) * (kHeadsPerTile / gh_max);
+int prefill_queries_per_item(int dtype, int head_dim, int gh_max) {
+  return prefill_col_tiles(dtype, head_dim) * (kHeadsPerTile / gh_max);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds, hipStream_t st) {

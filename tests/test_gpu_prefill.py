@@ -59,7 +59,10 @@ def test_prefill_of_one_token_matches_decode(cuda):
     dec = pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
                                     dev["context_lens"], x.scale, out_dtype=torch.float32, partition_size=-1)
     torch.cuda.synchronize()
-    assert torch.allclose(pre, dec, rtol=0, atol=2e-5)
+    # Both kernels split the weights the same way (bf16 value + remainder, rounded to nearest);
+    # they differ only in fp32 summation order and the exp2 argument's rounding.
+    diff = (pre - dec).abs().max().item()
+    assert diff <= 2e-5, diff
 
 
 def test_store_then_prefill_then_decode_chain(cuda):
