@@ -33,6 +33,8 @@
 
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -47,6 +49,13 @@ struct Piece {
   // workspace slot `slot` of range `rng`.
   static __device__ __forceinline__ void run(const DecodeArgs& a, int s, int r, int L, int lt0, int lt1,
                                              bool complete, int rng, int slot, int lane) {
+    // All of these are the same in every lane. Saying so lets the compiler keep what derives
+    // from them in scalar registers, and read the block table with scalar loads.
+    s = __builtin_amdgcn_readfirstlane(s);
+    r = __builtin_amdgcn_readfirstlane(r);
+    L = __builtin_amdgcn_readfirstlane(L);
+    lt0 = __builtin_amdgcn_readfirstlane(lt0);
+    lt1 = __builtin_amdgcn_readfirstlane(lt1);
     const int kq = lane >> 4;  // operand k-group, and result row group
     const int ln = lane & 15;  // operand row, and result column (= head in group)
     const int g = r / a.n_hg;
@@ -55,14 +64,14 @@ struct Piece {
     const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
     const int bs = a.block_size;
 
-    // Query operand: Q[h0 + ln][16-byte chunk 4j + kq]; zero for padding columns.
+    // Query operand: Q[h0 + ln][16-byte chunk 4j + kq]. The resource covers the group's gh
+    // head rows only, so padding columns (ln >= gh) read zeros, with no branch around the loads.
     u4 qv[C::kLoads];
     {
-      const char* qrow = reinterpret_cast<const char*>(a.q) +
-                         ((int64_t)s * a.q_seq_stride + (int64_t)(h0 + ln) * D) * C::kE;
+      const char* qg = reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.q_seq_stride + (int64_t)h0 * D) * C::kE;
+      const __amdgpu_buffer_rsrc_t qr = page_rsrc(qg, gh * D * C::kE);
 #pragma unroll
-      for (int j = 0; j < C::kLoads; ++j)
-        qv[j] = (ln < gh) ? *reinterpret_cast<const u4*>(qrow + (4 * j + kq) * 16) : u4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < C::kLoads; ++j) qv[j] = buf_load16<kPolicyDefault>(qr, ln * D * C::kE + (4 * j + kq) * 16);
     }
 
     f4 acc[C::kAcc];
@@ -85,9 +94,11 @@ struct Piece {
       const uint32_t k_lane = (uint32_t)((kq * bs + ln) * 16);
       const uint32_t v_lane = (DT == kF32) ? (uint32_t)((kq * D + ln) * 16) : (uint32_t)((kq * D + 2 * ln) * 8);
 
-      // Block-table entries, 64 pages at a time, one per lane.
-      int bt_first = INT32_MIN / 2;
-      int bt_val = 0;
+      // Block-table entries come from scalar loads (their own wait counter), one tile ahead.
+      // Tiles past the piece read the piece's last page entry and load nothing (below).
+      const_i32* cbt = (const_i32*)bt;
+      const int last_page = ((lt1 - 1) * kTile) >> a.bs_log2;
+      auto bt_entry = [&](int i) -> int { return cbt[min((i * kTile) >> a.bs_log2, last_page)]; };
 
       // Fused scatter (pa_decode_step): the step's new token sits at position L-1, in
       // row r0 of tile tl. The wavefront computing that tile takes its K/V from
@@ -111,38 +122,32 @@ struct Piece {
         }
       }
 
-      auto load_tile = [&](int i, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+      // Issues tile i's K/V loads with cache policy POL; raw = its page's block-table entry;
+      // t_hi = end of the tiles being streamed. Every loop position issues the same loads, so
+      // the compiler's wait counts stay exact and the next tile's loads stay in flight while
+      // this one is computed.
+      auto load_tile = [&](auto pol, int i, int raw, int t_hi, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+        constexpr int POL = decltype(pol)::value;
         const int t0 = i * kTile;
-        const int page = t0 >> a.bs_log2;
         const int off0 = t0 & (bs - 1);
-        if (page - bt_first >= 64 || page < bt_first) {
-          bt_first = page;
-          const int idx = page + lane;
-          bt_val = idx < a.max_blocks ? bt[idx] : 0;
-        }
-        int64_t blk = __builtin_amdgcn_readlane(bt_val, page - bt_first);
+        int64_t blk = __builtin_amdgcn_readfirstlane(raw);
         blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
         if (fuse && i == tl) blk_new = blk;
         // One buffer resource per page: the page's base in scalar registers,
-        // 32-bit lane offsets, and loads past the page end return zero.
-        const __amdgpu_buffer_rsrc_t kr = page_rsrc(kbase + blk * blk_stride, page_bytes32);
-        const __amdgpu_buffer_rsrc_t vr = page_rsrc(vbase + blk * blk_stride, page_bytes32);
+        // 32-bit lane offsets, and loads past the resource's end return zero. A tile past
+        // t_hi gets an empty resource: its loads return zeros and read no memory.
+        const int bytes = i < t_hi ? page_bytes32 : 0;
+        const __amdgpu_buffer_rsrc_t kr = page_rsrc(kbase + blk * blk_stride, bytes);
+        const __amdgpu_buffer_rsrc_t vr = page_rsrc(vbase + blk * blk_stride, bytes);
         const int koff = (int)k_lane + off0 * 16;
         const int voff = (int)v_lane + off0 * D * C::kE;
-        if (t0 >= a.cached_prefix_tokens) {
 #pragma unroll
-          for (int j = 0; j < C::kLoads; ++j) kb[j] = buf_load16<kPolicyStream>(kr, koff + j * 64 * bs);
+        for (int j = 0; j < C::kLoads; ++j) kb[j] = buf_load16<POL>(kr, koff + j * 64 * bs);
 #pragma unroll
-          for (int j = 0; j < C::kLoads; ++j) vb[j] = buf_load16<kPolicyStream>(vr, voff + j * 256);
-        } else {
-#pragma unroll
-          for (int j = 0; j < C::kLoads; ++j) kb[j] = buf_load16<kPolicyDefault>(kr, koff + j * 64 * bs);
-#pragma unroll
-          for (int j = 0; j < C::kLoads; ++j) vb[j] = buf_load16<kPolicyDefault>(vr, voff + j * 256);
-        }
+        for (int j = 0; j < C::kLoads; ++j) vb[j] = buf_load16<POL>(vr, voff + j * 256);
       };
 
-      auto compute_tile = [&](int i, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+      auto compute_tile = [&](int i, int t_hi, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
         if (fuse && i == tl) {
           const int i0 = r0 & 3;
           const bool krow = ln == r0, vrow = kq == (r0 >> 2);
@@ -197,15 +202,15 @@ struct Piece {
         }
         const int t0 = i * kTile;
         const bool partial = (t0 + kTile > L);
+        // past t_hi: a filler tile of the last round, every key masked
+        const int t_end = i < t_hi ? L : 0;
         float z[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           z[rr] = sv[rr] * a.scale_log2;
-          if (partial && (t0 + 4 * kq + rr >= L)) z[rr] = -INFINITY;
+          if ((partial || i >= t_hi) && (t0 + 4 * kq + rr >= t_end)) z[rr] = -INFINITY;
         }
-        float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mt = max_over_rows(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
         const float m_new = fmaxf(m, mt);
         const float alpha = exp2_fast(m - m_new);
         float p[4];
@@ -240,14 +245,16 @@ struct Piece {
             for (int e = 0; e < 4; ++e)
               acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb[u][e]), p[e], acc[u], 0, 0, 0);
         } else if constexpr (DT == kBF16) {
-          s4 ph, pl;
+          // Value + remainder, each rounded to nearest bf16 (two per packed conversion).
+          u2 hb, lb;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t hb = bf16_bits_rne(p[rr]);
-            const float rem = p[rr] - __uint_as_float(hb << 16);
-            ph[rr] = (short)hb;
-            pl[rr] = (short)bf16_bits_rne(rem);
+          for (int i2 = 0; i2 < 2; ++i2) {
+            hb[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{p[2 * i2], p[2 * i2 + 1]}, bf2));
+            const float r0 = p[2 * i2] - __uint_as_float(hb[i2] << 16);
+            const float r1 = p[2 * i2 + 1] - __uint_as_float(hb[i2] & 0xFFFF0000u);
+            lb[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf2));
           }
+          const s4 ph = __builtin_bit_cast(s4, hb), pl = __builtin_bit_cast(s4, lb);
 #pragma unroll
           for (int w = 0; w < C::kLoads; ++w) {
             const s4 a0 = __builtin_bit_cast(s4, u2{vb[w].x, vb[w].y});
@@ -277,41 +284,51 @@ struct Piece {
         }
       };
 
-      if constexpr (C::kPrefetch >= 2) {
-      // Three register sets in rotation: tiles i+1 and i+2 are in flight while tile i is computed.
-      u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads], kC[C::kLoads], vC[C::kLoads];
-      int i = lt0;
-      load_tile(i, kA, vA);
-      if (i + 1 < lt1) load_tile(i + 1, kB, vB);
-      while (true) {
-        if (i + 2 < lt1) load_tile(i + 2, kC, vC);
-        compute_tile(i, kA, vA);
-        if (i + 1 >= lt1) break;
-        if (i + 3 < lt1) load_tile(i + 3, kA, vA);
-        compute_tile(i + 1, kB, vB);
-        if (i + 2 >= lt1) break;
-        if (i + 4 < lt1) load_tile(i + 4, kB, vB);
-        compute_tile(i + 2, kC, vC);
-        if (i + 3 >= lt1) break;
-        i += 3;
-      }
-      } else {
-      // Two register sets: the loads of tile i+1 are in flight while tile i is computed.
-      u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads];
-      int i = lt0;
-      load_tile(i, kA, vA);
-      while (true) {
-        const bool has_b = i + 1 < lt1;
-        if (has_b) load_tile(i + 1, kB, vB);
-        compute_tile(i, kA, vA);
-        if (!has_b) break;
-        const bool has_a = i + 2 < lt1;
-        if (has_a) load_tile(i + 2, kA, vA);
-        compute_tile(i + 1, kB, vB);
-        if (!has_a) break;
-        i += 2;
-      }
-      }
+      // Streams tiles [t_lo, t_hi) with cache policy POL. One exit, at the bottom: a tile past
+      // t_hi that fills out the last round is loaded from an empty resource (zeros, no memory
+      // traffic) and masked out entirely. The next block-table read is issued after the load
+      // that uses the previous one, or waiting for that use would also wait for it.
+      auto stream = [&](auto pol, int t_lo, int t_hi) {
+        int raw_next = bt_entry(t_lo + 1);
+        auto issue = [&](int i, u4 (&kb)[C::kLoads], u4 (&vb)[C::kLoads]) {
+          load_tile(pol, i, raw_next, t_hi, kb, vb);
+          __builtin_amdgcn_sched_barrier(0);
+          raw_next = bt_entry(i + 1);
+        };
+        if constexpr (C::kPrefetch >= 2) {
+          // Three register sets in rotation: tiles i+1 and i+2 are in flight while tile i is computed.
+          u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads], kC[C::kLoads], vC[C::kLoads];
+          int i = t_lo;
+          load_tile(pol, i, bt_entry(i), t_hi, kA, vA);
+          issue(i + 1, kB, vB);
+          do {
+            issue(i + 2, kC, vC);
+            compute_tile(i, t_hi, kA, vA);
+            issue(i + 3, kA, vA);
+            compute_tile(i + 1, t_hi, kB, vB);
+            issue(i + 4, kB, vB);
+            compute_tile(i + 2, t_hi, kC, vC);
+            i += 3;
+          } while (i < t_hi);
+        } else {
+          // Two register sets: the loads of tile i+1 are in flight while tile i is computed.
+          u4 kA[C::kLoads], vA[C::kLoads], kB[C::kLoads], vB[C::kLoads];
+          int i = t_lo;
+          load_tile(pol, i, bt_entry(i), t_hi, kA, vA);
+          do {
+            issue(i + 1, kB, vB);
+            compute_tile(i, t_hi, kA, vA);
+            issue(i + 2, kA, vA);
+            compute_tile(i + 1, t_hi, kB, vB);
+            i += 2;
+          } while (i < t_hi);
+        }
+      };
+      // Tiles before cached_prefix_tokens with the default policy, the rest streamed: one loop
+      // per policy, since a per-tile choice between two load forms defeats the exact waits.
+      const int split = min(max((int)(((int64_t)a.cached_prefix_tokens + kTile - 1) / kTile), lt0), lt1);
+      if (lt0 < split) stream(std::integral_constant<int, kPolicyDefault>{}, lt0, split);
+      if (split < lt1) stream(std::integral_constant<int, kPolicyStream>{}, split, lt1);
     }
 
     // Sum of the four row groups' partial sums of each head column.

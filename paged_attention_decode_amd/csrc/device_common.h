@@ -29,6 +29,8 @@ typedef _Float16 h4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
 typedef _Float16 h8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef __bf16 b8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef unsigned int u2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 template <int DT, int D>
 struct Cfg {

@@ -57,8 +57,6 @@ struct PrefillCfg {
   static constexpr int kNC = prefill_col_tiles(DT, D);
 };
 
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-typedef float fl2 __attribute__((ext_vector_type(2)));
 
 template <int DT, int D>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g, int hg, int qb, int lane) {
@@ -309,11 +307,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
           // gfx950 rounds two floats to bf16 (nearest even) in one instruction.
 #pragma unroll
           for (int i2 = 0; i2 < 4; ++i2) {
-            const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(fl2{p[2 * i2], p[2 * i2 + 1]}, bf2));
+            const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{p[2 * i2], p[2 * i2 + 1]}, bf2));
             const float r0 = p[2 * i2] - __uint_as_float(hb << 16);
             const float r1 = p[2 * i2 + 1] - __uint_as_float(hb & 0xFFFF0000u);
             ph[i2] = hb;
-            pl[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(fl2{r0, r1}, bf2));
+            pl[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf2));
           }
         } else {
 #pragma unroll
