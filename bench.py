@@ -61,6 +61,8 @@ def parse():
                     help="also time a PyTorch gather-and-mask decode on the same inputs (benchmark only)")
     ap.add_argument("--cold-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush each")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-timings", action="store_true",
+                    help="skip the per-call and per-mode timings (profiled runs: only the timed steps launch)")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="target seconds of oracle work")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/decode_<workload>_traffic.txt from two rocprofv3 --pmc runs "
@@ -502,10 +504,12 @@ def main():
              "decode": decode_with(args.partition_size), "store_plus_decode": step}
     for psize, name in ((0, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
         calls[name] = decode_with(psize)
-    timings = extra_timings(calls, 20, 2 << 30, dev)
-    timings["decode_tokens_per_s"] = round(cfg.batch / (timings["decode"]["median_us"] * 1e-6), 1)
-    timings["note"] = ("cudaEvent pairs per call on the current stream, back to back (warm caches); "
-                       "decode includes the merge kernel where the plan splits")
+    timings = None
+    if not args.no_extra_timings:
+        timings = extra_timings(calls, 20, 2 << 30, dev)
+        timings["decode_tokens_per_s"] = round(cfg.batch / (timings["decode"]["median_us"] * 1e-6), 1)
+        timings["note"] = ("cudaEvent pairs per call on the current stream, back to back (warm caches); "
+                           "decode includes the merge kernel where the plan splits")
 
     traffic = traffic_from_profiles(cfg.name, kv_bytes)
     result = {
@@ -526,7 +530,8 @@ def main():
                      "kernel_mean_ms": round(mean_kernel_ms, 5),
                      "cold_kernel_median_ms": round(sorted(cold)[len(cold) // 2], 5) if cold else None},
     }
-    result["timings"] = timings
+    if timings:
+        result["timings"] = timings
     if comparators:
         result["comparators"] = comparators
     if not args.no_cpu_baseline:
