@@ -53,11 +53,20 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Maximum over lanes l, l^16, l^32 and l^48 (the four 16-lane rows), with gfx950's row-swap
 // instructions: each swap leaves lane l's value and its partner's in the two results.
+// The maxima are IEEE-2019 `maximum` (gfx950 has it natively, with a three-input form): unlike
+// fmaxf it needs no NaN-quieting instruction on inputs the compiler cannot prove canonical, such
+// as matrix-core results.
 __device__ __forceinline__ float max_over_rows(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float fmax8(const float (&x)[8]) {
+  const float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]);
+  const float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], x[4]), x[5]);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), __builtin_elementwise_maximum(x[6], x[7]));
 }
 
 // Read-only view of a table that no kernel writes while it runs (block tables): uniform reads

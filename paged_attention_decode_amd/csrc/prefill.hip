@@ -276,17 +276,20 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
           if (t > pos[ct]) x[j] = -INFINITY;
         }
       }
-      float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      // IEEE-2019 maximum: gfx950 has a three-input form, and it needs no NaN quieting first.
+      float mt = fmax8(x);
       mt = max_over_rows(mt);
-      // Key 0 is visible to every column, so m is finite from the first step on.
-      const float m_new = fmaxf(m[ct], mt * c);
-      const float alpha = exp2_fast(m[ct] - m_new);
+      // Key 0 is visible to every column, so m is finite from the first step on. The running
+      // maximum is kept unless it grew by more than 8 (log2 units): weights stay below 2^8,
+      // and the accumulators are rescaled only on such jumps instead of on every new maximum.
+      const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
+      const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
+      const float alpha = exp2_fast(m[ct] - m_use);
       float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, -m_new));
+      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, -m_use));
       l[ct] = fmaf(l[ct], alpha, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-      m[ct] = m_new;
-      // Rescale only when some column's running maximum moved in this step.
+      m[ct] = m_use;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
         for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha;
