@@ -39,6 +39,10 @@ int ok() {
 #define PA_GROUPS_PER_CU 2
 #endif
 constexpr int kGroupsPerCU = PA_GROUPS_PER_CU;
+#ifndef PA_PREFILL_SHARED
+#define PA_PREFILL_SHARED 1
+#endif
+constexpr bool kPrefillShared = PA_PREFILL_SHARED != 0;
 
 struct DeviceState {
   bool init = false;
@@ -276,14 +280,31 @@ int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache,
   a.max_blocks = max_blocks_per_seq;
   a.out_f32 = out_dtype == PA_DTYPE_F32 ? 1 : 0;
   const int qpi = prefill_queries_per_item(dtype, head_dim, a.gh_max);
-  const int64_t items = (int64_t)num_kv_heads * a.n_hg * (((int64_t)num_tokens + qpi - 1) / qpi + num_seqs);
-  const int64_t resident = (int64_t)st->num_cus * kGroupsPerCU * kWavesPerGroup;
-  int64_t waves = items < resident ? items : resident;
-  if (waves < 1) waves = 1;
-  const int grid = (int)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
-  a.num_waves = grid * kWavesPerGroup;
-  hipError_t err = launch_prefill(a, dtype, head_dim, grid, (size_t)(num_seqs + 1) * sizeof(int32_t),
-                                  reinterpret_cast<hipStream_t>(stream));
+  const size_t prefix_bytes = (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int32_t);
+  hipError_t err;
+  // 16-bit inputs at head_dim 128: four wavefronts share each K/V step through LDS (a quarter of
+  // the L2 traffic, which bounds the per-wavefront kernel there). At head_dim 64 the per-wavefront
+  // kernel is bound by its arithmetic instead and is faster; it also serves fp32, head_dim 256,
+  // and batches whose item prefix would push the shared kernel's LDS past 64 KiB.
+  const size_t shared_lds = prefix_bytes + prefill_shared_buffer_bytes(head_dim);
+  if (kPrefillShared && dtype != PA_DTYPE_F32 && head_dim == 128 && shared_lds <= 65536) {
+    const int wq = kWavesPerGroup * qpi;
+    const int64_t items = (int64_t)num_kv_heads * a.n_hg * (((int64_t)num_tokens + wq - 1) / wq + num_seqs);
+    const int64_t resident = (int64_t)st->num_cus * kGroupsPerCU;
+    int64_t grid = items < resident ? items : resident;
+    if (grid < 1) grid = 1;
+    a.num_waves = (int)grid * kWavesPerGroup;
+    err = launch_prefill_shared(a, dtype, head_dim, (int)grid, shared_lds, reinterpret_cast<hipStream_t>(stream));
+  } else {
+    const int64_t items = (int64_t)num_kv_heads * a.n_hg * (((int64_t)num_tokens + qpi - 1) / qpi + num_seqs);
+    const int64_t resident = (int64_t)st->num_cus * kGroupsPerCU * kWavesPerGroup;
+    int64_t waves = items < resident ? items : resident;
+    if (waves < 1) waves = 1;
+    const int grid = (int)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
+    a.num_waves = grid * kWavesPerGroup;
+    err = launch_prefill(a, dtype, head_dim, grid, (size_t)(num_seqs + 1) * sizeof(int32_t),
+                         reinterpret_cast<hipStream_t>(stream));
+  }
   if (err != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
   return ok();
 }

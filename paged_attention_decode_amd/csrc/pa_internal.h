@@ -101,8 +101,13 @@ struct PrefillArgs {
 // Launchers (return the launch error, hipSuccess otherwise).
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
                           hipStream_t stream);
-// Query tokens one prefill work item covers.
+// Query tokens one prefill work item covers (per wavefront; a shared-variant workgroup covers
+// kWavesPerGroup times as many).
 int prefill_queries_per_item(int dtype, int head_dim, int gh_max);
+// Workgroup-shared prefill (16-bit inputs, head_dim 128): its two LDS step buffers.
+size_t prefill_shared_buffer_bytes(int head_dim);
+hipError_t launch_prefill_shared(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
+                                 hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
                          hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);

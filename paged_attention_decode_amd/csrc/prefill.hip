@@ -44,11 +44,14 @@ using namespace dev;
 #ifndef PA_PREFILL_NC64
 #define PA_PREFILL_NC64 4
 #endif
+#ifndef PA_PREFILL_NC128
+#define PA_PREFILL_NC128 2
+#endif
 
 // Column tiles per wavefront: every K/V load serves 16 * col_tiles columns.
 constexpr int prefill_col_tiles(int dtype, int head_dim) {
   return dtype == kF32 ? (head_dim <= 64 ? 2 : 1)
-                       : (head_dim <= 64 ? PA_PREFILL_NC64 : (head_dim <= 128 ? 2 : 1));
+                       : (head_dim <= 64 ? PA_PREFILL_NC64 : (head_dim <= 128 ? PA_PREFILL_NC128 : 1));
 }
 
 template <int DT, int D>
@@ -375,23 +378,21 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   }
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillArgs a) {
-  extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]: first work item of each sequence
-  __shared__ int32_t s_wsum[kWavesPerGroup];
-  constexpr int NC = PrefillCfg<DT, D>::kNC;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that consecutive
-  // waves, which take consecutive items, run on one XCD and share its L2.
+// Workgroups are dealt round-robin to the 8 XCDs; renumbered this way, consecutive numbers
+// (which take consecutive work items) run on one XCD and share its L2.
+__device__ __forceinline__ int xcd_group() {
   int grp = blockIdx.x;
   if ((gridDim.x & 7) == 0) grp = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int wave = grp * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int max_len = a.max_blocks << a.bs_log2;
-  const int qb_queries = NC * (kHeadsPerTile / a.gh_max);
-  const int H = a.num_kv_heads * a.n_hg;
+  return grp;
+}
 
-  // Items per sequence: ceil(n / queries per block) * kv heads * head groups.
+// s_prefix[i] = first work item of sequence i, where a sequence has ceil(n / queries_per_item)
+// items per (kv head, head group); n = its new tokens. Returns the total. All threads call it.
+__device__ int build_item_prefix(const PrefillArgs& a, int queries_per_item, int32_t* s_prefix, int32_t* s_wsum) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int max_len = a.max_blocks << a.bs_log2;
+  const int H = a.num_kv_heads * a.n_hg;
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += kDecodeThreads) {
     const int i = base + tid;
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
       L = L < 0 ? 0 : (L > max_len ? max_len : L);
       int n = a.query_start[i + 1] - a.query_start[i];
       n = n < 0 ? 0 : (n > L ? L : n);
-      v = ((n + qb_queries - 1) / qb_queries) * H;
+      v = ((n + queries_per_item - 1) / queries_per_item) * H;
     }
     int x = v;
 #pragma unroll
@@ -424,7 +425,21 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
   }
   if (tid == 0) s_prefix[0] = 0;
   __syncthreads();
-  const int total = s_prefix[a.num_seqs];
+  return s_prefix[a.num_seqs];
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillArgs a) {
+  extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]: first work item of each sequence
+  __shared__ int32_t s_wsum[kWavesPerGroup];
+  constexpr int NC = PrefillCfg<DT, D>::kNC;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = xcd_group() * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb_queries = NC * (kHeadsPerTile / a.gh_max);
+  const int H = a.num_kv_heads * a.n_hg;
+
+  const int total = build_item_prefix(a, qb_queries, s_prefix, s_wsum);
 
   for (int item = wave; item < total; item += a.num_waves) {
     int lo = 0, hi = a.num_seqs;
@@ -444,6 +459,331 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Workgroup-shared variant (16-bit inputs, head_dim 128). The four wavefronts of a workgroup take four
+// consecutive query blocks of one (sequence, kv head, head group), so they need the same keys.
+// Each 32-key step is loaded once per workgroup: wavefront 0 loads K of the step's first tile,
+// 1 K of the second, 2 and 3 the V tiles; they store them to LDS (double-buffered, one barrier
+// per step) and every wavefront reads its matrix-core operands from there. Per step that is a
+// quarter of the K/V traffic from L2 of the per-wavefront kernel, which at head_dim 128 is
+// bound by exactly that traffic.
+//
+// LDS buffer of one step (T = one 16-key tile of K or V, 16 * D * 2 bytes):
+//   [0, T)     K tile A, as 16-byte operand chunks in lane order: (j * 64 + lane) * 16
+//   [T, 2T)    K tile B, the same
+//   [2T, 4T)   V: 16-byte slots (kq * D + d): bytes 0-7 = keys 4kq .. 4kq+3 of dim d in tile A,
+//              bytes 8-15 the same in tile B. Lane (kq, ln) reads the second product's operands
+//              for dims 32w + ln and 32w + 16 + ln as slots (kq * D + 32w + ln) and (... + 16).
+template <int DT, int D>
+struct SharedCfg {
+  using C = Cfg<DT, D>;
+  static constexpr int kNC = prefill_col_tiles(DT, D);
+  static constexpr int kTileBytes = kTile * D * C::kE;
+  static constexpr int kBufBytes = 4 * kTileBytes;
+};
+
+template <int DT, int D>
+__device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s, int g, int hg, int qbg, int wv,
+                                                    int lane, char* lds) {
+  using C = Cfg<DT, D>;
+  using SC = SharedCfg<DT, D>;
+  static_assert(DT != kF32, "the shared variant takes 16-bit inputs");
+  constexpr int NC = SC::kNC;
+  constexpr int T = SC::kTileBytes;
+  const int kq = lane >> 4;
+  const int ln = lane & 15;
+  const int bs = a.block_size;
+  const int max_len = a.max_blocks << a.bs_log2;
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > max_len ? max_len : L);
+  const int q0 = a.query_start[s];
+  int n = a.query_start[s + 1] - q0;
+  n = n < 0 ? 0 : (n > L ? L : n);
+  const int gh = a.gh_max;
+  const int qpt = kHeadsPerTile / gh;
+  const int qb_queries = NC * qpt;
+  // The workgroup's queries and keys (the same in every wavefront).
+  const int wg_first = qbg * kWavesPerGroup * qb_queries;
+  const int wg_last = min(n, wg_first + kWavesPerGroup * qb_queries) - 1;
+  const int p_last_wg = L - n + wg_last;
+  // This wavefront's query block; a workgroup at the end of a sequence may have idle wavefronts,
+  // which still load their share and meet every barrier.
+  const int qfirst = wg_first + wv * qb_queries;
+  const bool active = qfirst < n;
+  const int p_first = L - n + qfirst;
+
+  int qi[NC], hh[NC], pos[NC];
+  bool valid[NC];
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) {
+    const int ql = ln / gh;
+    const int hl = hg * kHeadsPerTile + (ln % gh);
+    qi[ct] = qfirst + ct * qpt + ql;
+    hh[ct] = g * a.group + hl;
+    valid[ct] = active && ql < qpt && hl < a.group && qi[ct] < n;
+    pos[ct] = valid[ct] ? L - n + qi[ct] : p_last_wg;
+  }
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float c = fmaxf(fabsf(a.scale_log2), FLT_MIN);
+  u4 qv[NC][C::kLoads];
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) {
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       ((int64_t)(q0 + qi[ct]) * a.q_token_stride + (int64_t)hh[ct] * D) * C::kE;
+#pragma unroll
+    for (int j = 0; j < C::kLoads; ++j) {
+      qv[ct][j] = valid[ct] ? *reinterpret_cast<const u4*>(qrow + (4 * j + kq) * 16) : u4{0u, 0u, 0u, 0u};
+      qv[ct][j] ^= u4{qflip, qflip, qflip, qflip};
+    }
+  }
+  f4 acc[NC][C::kAcc];
+  float m[NC], l[NC];
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) {
+    m[ct] = -INFINITY;
+    l[ct] = 0.f;
+#pragma unroll
+    for (int u = 0; u < C::kAcc; ++u) acc[ct][u] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int64_t page_bytes = (int64_t)bs * D * C::kE;
+  const int page_bytes32 = (int)page_bytes;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * page_bytes;
+  const int64_t nb_max = a.num_blocks - 1;
+  const int tiles = p_last_wg / kTile + 1;
+  const int steps = (tiles + 1) >> 1;
+  const_i32* cbt = (const_i32*)(a.block_tables + (int64_t)s * a.max_blocks);
+
+  // This wavefront's share of each step: K (wv < 2) or V (wv >= 2) of tile A (even wv) or B.
+  // The same instructions for every share (the base and lane offsets are selected), so each
+  // wavefront's loads are unconditional and the compiler's wait counts stay exact.
+  const bool share_k = wv < 2;
+  const int half = wv & 1;
+  const char* sbase = reinterpret_cast<const char*>(share_k ? a.k_cache : a.v_cache) + (int64_t)g * page_bytes;
+  // K: chunk (4j + kq) of token (off0 + ln); V: tokens off0 + 4kq .. +3 of dims 32j + 2ln, +1.
+  const int lane_off = share_k ? (kq * bs + ln) * 16 : (kq * D + 2 * ln) * 8;
+  const int j_stride = share_k ? 64 * bs : 256;
+  const int off_per_key = share_k ? 16 : D * C::kE;
+  auto share_tile = [&](int st) { return min(2 * st + half, tiles - 1); };
+  u4 stg[C::kLoads];
+  auto load_share = [&](int st, int raw) {
+    const int tile = share_tile(st);
+    int64_t blk = __builtin_amdgcn_readfirstlane(raw);
+    blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
+    // A tile that does not exist (an odd last step) loads zeros and reads no memory.
+    const int bytes = 2 * st + half < tiles ? page_bytes32 : 0;
+    const __amdgpu_buffer_rsrc_t r = page_rsrc(sbase + blk * blk_stride, bytes);
+    const int off = lane_off + ((tile * kTile) & (bs - 1)) * off_per_key;
+#pragma unroll
+    for (int j = 0; j < C::kLoads; ++j) stg[j] = buf_load16<kPolicyDefault>(r, off + j * j_stride);
+  };
+  auto bt_entry = [&](int st) -> int {
+    return cbt[(share_tile(min(st, steps - 1)) * kTile) >> a.bs_log2];
+  };
+  // Values of keys at or beyond L may be anything: zero them before they are shared.
+  auto store_share = [&](int st, char* buf) {
+    if (share_k) {
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) *reinterpret_cast<u4*>(buf + half * T + (j * 64 + lane) * 16) = stg[j];
+    } else {
+      const int t0 = share_tile(st) * kTile;
+      if (t0 + kTile > L) {
+        const bool v0 = t0 + 4 * kq + 0 < L, v1 = t0 + 4 * kq + 1 < L;
+        const bool v2 = t0 + 4 * kq + 2 < L, v3 = t0 + 4 * kq + 3 < L;
+        const uint32_t m01 = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (v2 ? 0x0000FFFFu : 0u) | (v3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j) stg[j] &= u4{m01, m23, m01, m23};
+      }
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) {
+        char* v = buf + 2 * T + (kq * D + 32 * j + 2 * ln) * 16 + half * 8;
+        *reinterpret_cast<u2*>(v) = u2{stg[j].x, stg[j].y};
+        *reinterpret_cast<u2*>(v + 16) = u2{stg[j].z, stg[j].w};
+      }
+    }
+  };
+
+  int raw_next = bt_entry(1);
+  load_share(0, bt_entry(0));
+  store_share(0, lds);
+  __syncthreads();
+  for (int st = 0; st < steps; ++st) {
+    char* buf = lds + (st & 1) * SC::kBufBytes;
+    // Next step's share: in flight during this step's arithmetic (re-reads the last step at the end).
+    load_share(st + 1, raw_next);
+    __builtin_amdgcn_sched_barrier(0);
+    raw_next = bt_entry(st + 2);
+
+    if (active) {
+      const int t0 = st * 2 * kTile;
+      u4 kA[C::kLoads], kB[C::kLoads];
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) {
+        kA[j] = *reinterpret_cast<const u4*>(buf + (j * 64 + lane) * 16);
+        kB[j] = *reinterpret_cast<const u4*>(buf + T + (j * 64 + lane) * 16);
+      }
+      f4 sA[NC], sB[NC];
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        sA[ct] = f4{0.f, 0.f, 0.f, 0.f};
+        sB[ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j) {
+          if constexpr (DT == kBF16) {
+            sA[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, kA[j]),
+                                                             __builtin_bit_cast(b8, qv[ct][j]), sA[ct], 0, 0, 0);
+            sB[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, kB[j]),
+                                                             __builtin_bit_cast(b8, qv[ct][j]), sB[ct], 0, 0, 0);
+          } else {
+            sA[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kA[j]),
+                                                            __builtin_bit_cast(h8, qv[ct][j]), sA[ct], 0, 0, 0);
+            sB[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kB[j]),
+                                                            __builtin_bit_cast(h8, qv[ct][j]), sB[ct], 0, 0, 0);
+          }
+        }
+      }
+      u4 va0[C::kLoads], va1[C::kLoads];
+#pragma unroll
+      for (int w = 0; w < C::kLoads; ++w) {
+        va0[w] = *reinterpret_cast<const u4*>(buf + 2 * T + (kq * D + 32 * w + ln) * 16);
+        va1[w] = *reinterpret_cast<const u4*>(buf + 2 * T + (kq * D + 32 * w + 16 + ln) * 16);
+      }
+      const bool open = t0 + 2 * kTile - 1 <= p_first;
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        float x[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = sA[ct][r];
+          x[4 + r] = sB[ct][r];
+        }
+        if (!open) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int t = t0 + (j < 4 ? 0 : kTile) + 4 * kq + (j & 3);
+            if (t > pos[ct]) x[j] = -INFINITY;
+          }
+        }
+        const float mt = max_over_rows(fmax8(x));
+        // Key 0 is visible to every column; the running maximum moves only on jumps above 8.
+        const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
+        const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
+        const float alpha = exp2_fast(m[ct] - m_use);
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, -m_use));
+        l[ct] = fmaf(l[ct], alpha, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        m[ct] = m_use;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+          for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha;
+        }
+        u4 ph, pl;
+        if constexpr (DT == kBF16) {
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{p[2 * i2], p[2 * i2 + 1]}, bf2));
+            const float r0 = p[2 * i2] - __uint_as_float(hb << 16);
+            const float r1 = p[2 * i2 + 1] - __uint_as_float(hb & 0xFFFF0000u);
+            ph[i2] = hb;
+            pl[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf2));
+          }
+        } else {
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            const auto hv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2], p[2 * i2 + 1]);
+            const auto lv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2] - (float)hv[0], p[2 * i2 + 1] - (float)hv[1]);
+            ph[i2] = __builtin_bit_cast(uint32_t, hv);
+            pl[i2] = __builtin_bit_cast(uint32_t, lv);
+          }
+        }
+#pragma unroll
+        for (int w = 0; w < C::kLoads; ++w) {
+          if constexpr (DT == kBF16) {
+            const b8 bh = __builtin_bit_cast(b8, ph), bl = __builtin_bit_cast(b8, pl);
+            const b8 a0 = __builtin_bit_cast(b8, va0[w]), a1 = __builtin_bit_cast(b8, va1[w]);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, acc[ct][2 * w + 1], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc[ct][2 * w + 1], 0, 0, 0);
+          } else {
+            const h8 hh8 = __builtin_bit_cast(h8, ph), hl8 = __builtin_bit_cast(h8, pl);
+            const h8 a0 = __builtin_bit_cast(h8, va0[w]), a1 = __builtin_bit_cast(h8, va1[w]);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hh8, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hl8, acc[ct][2 * w], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hh8, acc[ct][2 * w + 1], 0, 0, 0);
+            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hl8, acc[ct][2 * w + 1], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // The other buffer was last read in the previous step, before its barrier.
+    store_share(st + 1, lds + ((st + 1) & 1) * SC::kBufBytes);
+    __syncthreads();
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) {
+    float lt = l[ct] + __shfl_xor(l[ct], 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    if (!valid[ct]) continue;
+    const int64_t base = ((int64_t)(q0 + qi[ct]) * a.num_heads + hh[ct]) * D;
+#pragma unroll
+    for (int w = 0; w < C::kLoads; ++w) {
+      const float v0[4] = {acc[ct][2 * w][0] * inv, acc[ct][2 * w][1] * inv, acc[ct][2 * w][2] * inv,
+                           acc[ct][2 * w][3] * inv};
+      const float v1[4] = {acc[ct][2 * w + 1][0] * inv, acc[ct][2 * w + 1][1] * inv, acc[ct][2 * w + 1][2] * inv,
+                           acc[ct][2 * w + 1][3] * inv};
+      store4<DT>(a.out, base + 32 * w + 4 * kq, v0, a.out_f32 != 0);
+      store4<DT>(a.out, base + 32 * w + 16 + 4 * kq, v1, a.out_f32 != 0);
+    }
+  }
+}
+
+// Workgroup-level items: (sequence, kv head, head group, group of four query blocks), on
+// persistent workgroups. Dynamic LDS: the item prefix ([num_seqs + 1] ints, rounded up to 16
+// bytes), then two step buffers.
+template <int DT, int D>
+__global__ __launch_bounds__(kDecodeThreads) void prefill_shared_kernel(const PrefillArgs a) {
+  extern __shared__ __align__(16) int32_t s_dyn[];
+  __shared__ int32_t s_wsum[kWavesPerGroup];
+  constexpr int NC = SharedCfg<DT, D>::kNC;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = xcd_group();
+  const int wg_queries = kWavesPerGroup * NC * (kHeadsPerTile / a.gh_max);
+  const int H = a.num_kv_heads * a.n_hg;
+  int32_t* s_prefix = s_dyn;
+  char* bufs = reinterpret_cast<char*>(s_dyn + ((a.num_seqs + 1 + 3) & ~3));
+  const int total = build_item_prefix(a, wg_queries, s_prefix, s_wsum);
+  for (int item = grp; item < total; item += gridDim.x) {
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_prefix[mid] <= item) lo = mid; else hi = mid;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int local = item - s_prefix[s];
+    const int nqb = (s_prefix[s + 1] - s_prefix[s]) / H;
+    const int r = local / nqb;
+    const int qbg = __builtin_amdgcn_readfirstlane(nqb - 1 - (local - r * nqb));
+    const int rr = __builtin_amdgcn_readfirstlane(r);
+    prefill_shared_item<DT, D>(a, s, rr / a.n_hg, rr % a.n_hg, qbg, wv, lane, bufs);
+    // The next item's first store goes to buffer 0, which this item may have read last.
+    __syncthreads();
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_prefill_shared_t(const PrefillArgs& a, int grid, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_shared_kernel<DT, D>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_prefill_t(const PrefillArgs& a, int grid, size_t lds, hipStream_t st) {
   hipLaunchKernelGGL((prefill_kernel<DT, D>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
@@ -454,6 +794,18 @@ hipError_t launch_prefill_t(const PrefillArgs& a, int grid, size_t lds, hipStrea
 
 int prefill_queries_per_item(int dtype, int head_dim, int gh_max) {
   return prefill_col_tiles(dtype, head_dim) * (kHeadsPerTile / gh_max);
+}
+
+size_t prefill_shared_buffer_bytes(int head_dim) {
+  return 2 * 4 * (size_t)kTile * head_dim * 2;
+}
+
+hipError_t launch_prefill_shared(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds,
+                                 hipStream_t st) {
+  if (head_dim != 128) return hipErrorInvalidValue;
+  if (dtype == kF16) return launch_prefill_shared_t<kF16, 128>(a, grid, lds, st);
+  if (dtype == kBF16) return launch_prefill_shared_t<kBF16, 128>(a, grid, lds, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds, hipStream_t st) {

@@ -23,6 +23,8 @@ CASES = [
     ("bf16", 40, 2, 64, 16, (70, 31), (70, 2)),                   # G = 20: head groups 16 + 4
     ("fp16", 6, 2, 256, 64, (90, 130), (90, 17)),                 # odd G, head_dim 256
     ("bf16", 8, 2, 128, 16, (5, 0, 30), (5, 0, 30)),              # an empty sequence
+    ("bf16", 16, 8, 128, 16, (700, 333), (700, 100)),             # many workgroup items per sequence
+    ("fp16", 8, 8, 64, 32, (257, 64, 3), (257, 64, 3)),           # G = 1, partly idle workgroups
 ]
 
 
@@ -96,3 +98,28 @@ def test_store_then_prefill_then_decode_chain(cuda):
         ref = oracle.decode_sequence(qf[i], kd[:i + 1], vd[:i + 1], 0.1)
         got = pre[i].cpu().numpy() if i < prompt else step[0].cpu().numpy()
         assert np.abs(got - ref).max() <= 2e-3, i
+
+
+def test_prefill_of_many_sequences_uses_the_per_wavefront_kernel(cuda):
+    """8200 sequences: the shared variant's LDS (item prefix + step buffers) would pass 64 KiB, so
+    the library takes the per-wavefront kernel; both must agree with the oracle."""
+    import torch
+    import paged_attention_decode_amd as pa
+    rng = np.random.default_rng(77)
+    lens = tuple(int(v) for v in rng.integers(1, 5, 8200))
+    x = make_inputs(custom_config(dtype="bf16", batch=len(lens), hq=8, hkv=2, d=128, bs=16, lens=lens, seed=77))
+    news = lens
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = to_storage(rng.standard_normal((int(qs[-1]), 8, 128), dtype=np.float32), "bf16")
+    dev = to_device(x, cuda)
+    print(f"[gpu] prefill of {len(lens)} sequences", flush=True)
+    out = pa.paged_prefill(np_to_torch(q, "bf16").to(cuda), dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                           dev["context_lens"], torch.from_numpy(qs).to(cuda), x.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    seqs = range(0, len(lens), 97)
+    ref = oracle.prefill(q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, qs, x.scale, geometry(x),
+                         seqs=list(seqs))
+    for s_ in seqs:
+        rows = slice(qs[s_], qs[s_ + 1])
+        assert np.abs(out[rows] - ref[rows]).max() <= TOL["bf16"], s_
