@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--partition-size", type=int, default=0, help="0 balanced split, -1 one pass, >0 fixed")
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="0 automatic, -1 one pass, -2 balanced split, >0 fixed ranges of that many tokens")
     ap.add_argument("--cached-prefix-tokens", type=int, default=0,
                     help="leading tokens per context read with cached loads (0 library default, -1 none)")
     ap.add_argument("--fused-step", action="store_true",
@@ -502,7 +503,7 @@ def main():
                                                  cached_prefix_tokens=args.cached_prefix_tokens)
     calls = {"store": lambda: pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache),
              "decode": decode_with(args.partition_size), "store_plus_decode": step}
-    for psize, name in ((0, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
+    for psize, name in ((-2, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
         calls[name] = decode_with(psize)
     timings = None
     if not args.no_extra_timings:

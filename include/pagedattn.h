@@ -161,12 +161,15 @@ int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_
  * Options for pa_paged_attention_decode_ex.
  *
  * partition_size (tokens):
- *    0  automatic: the concatenated 16-token tiles of all (sequence, kv head)
- *       contexts are divided evenly over the wavefronts the device holds at
- *       once, so long and short sequences finish together; contexts cut by a
- *       range boundary are merged by the reduce kernel.
+ *    0  automatic: one pass (-1) when no context can exceed 512 tokens
+ *       (max_blocks_per_seq * block_size <= 512), balanced ranges (-2)
+ *       otherwise. Decided on the host from the sizes alone.
  *   -1  one pass: every (sequence, kv head) context is handled whole by one
  *       wavefront; no reduce kernel runs.
+ *   -2  balanced ranges: the concatenated 16-token tiles of all (sequence,
+ *       kv head) contexts are divided evenly over the wavefronts the device
+ *       holds at once, so long and short sequences finish together; contexts
+ *       cut by a range boundary are merged by the reduce kernel.
  *   >0  fixed ranges of partition_size tokens (a multiple of 16) over the same
  *       concatenated tile stream. The device's resident wavefronts loop over
  *       the ranges; the workspace has rows for the ranges of the longest

@@ -43,6 +43,9 @@ constexpr int kGroupsPerCU = PA_GROUPS_PER_CU;
 #define PA_PREFILL_SHARED 1
 #endif
 constexpr bool kPrefillShared = PA_PREFILL_SHARED != 0;
+// partition_size values: 0 automatic, -1 one pass, -2 balanced ranges, > 0 fixed ranges.
+constexpr int kBalanced = -2;
+constexpr int64_t kOnePassMaxTokens = 512;
 
 struct DeviceState {
   bool init = false;
@@ -95,8 +98,8 @@ int check_decode_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   if (max_blocks <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks);
   if ((int64_t)max_blocks * block_size > INT32_MAX / 2)
     return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size too large");
-  if (partition_size < -1 || (partition_size > 0 && partition_size % kTile != 0))
-    return fail(PA_ERR_SHAPE, "partition_size %d must be -1, 0 or a positive multiple of 16", partition_size);
+  if (partition_size < -2 || (partition_size > 0 && partition_size % kTile != 0))
+    return fail(PA_ERR_SHAPE, "partition_size %d must be -2, -1, 0 or a positive multiple of 16", partition_size);
   return PA_OK;
 }
 
@@ -111,7 +114,13 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
   const int64_t upper_tiles = segs * (max_tiles > 0 ? max_tiles : 1);
   const int64_t resident = (int64_t)num_cus * kGroupsPerCU * kWavesPerGroup;
   int64_t waves;
-  if (partition_size < 0) {
+  // Automatic: one pass when no context can be longer than kOnePassMaxTokens (the host's bound,
+  // max_blocks * block_size; it reads no device memory): every segment is then short, one
+  // wavefront per segment finishes about as soon as balanced ranges would, and no merge kernel
+  // runs. Otherwise balanced ranges.
+  if (partition_size == 0)
+    partition_size = (int64_t)max_blocks * block_size <= kOnePassMaxTokens ? -1 : kBalanced;
+  if (partition_size == -1) {
     p->range_tiles = -1;
     waves = segs < resident ? segs : resident;
     p->lds = 0;
@@ -121,7 +130,7 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
       return fail(PA_ERR_UNSUPPORTED, "batch too large: %lld tiles", (long long)upper_tiles);
     p->lds = (size_t)(num_seqs + 1) * sizeof(int32_t);
     p->reduce = true;
-    if (partition_size == 0) {
+    if (partition_size == kBalanced) {
       // One range per wavefront, sized on the device from the actual lengths.
       p->range_tiles = 0;
       const int64_t useful = (upper_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave;

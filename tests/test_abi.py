@@ -87,8 +87,21 @@ def test_plan_fixed_ranges_loop_on_resident_waves():
 
 
 def test_plan_small_batch_does_not_oversubscribe():
-    p = _plan(num_seqs=4, num_heads=4, num_kv_heads=2, head_dim=64, max_blocks_per_seq=4, dtype_code=pa.DTYPE_F32)
+    p = _plan(num_seqs=4, num_heads=4, num_kv_heads=2, head_dim=64, max_blocks_per_seq=4, dtype_code=pa.DTYPE_F32,
+              partition_size=-2)
+    assert p["range_tokens"] == 0 and p["uses_reduce"]
     assert p["num_waves"] <= 16  # 32 tiles at most, at least 2 tiles per wavefront
+
+
+@pytest.mark.parametrize("mb,bs,one_pass", [(32, 16, True), (2, 256, True), (33, 16, False), (4, 256, False),
+                                            (1024, 16, False)])
+def test_plan_automatic_takes_one_pass_for_short_bounded_contexts(mb, bs, one_pass):
+    # the host's only bound on a context is max_blocks_per_seq * block_size: one pass up to 512 tokens
+    p = _plan(max_blocks_per_seq=mb, block_size=bs)
+    assert (p["range_tokens"] == -1) == one_pass
+    assert p["uses_reduce"] != one_pass
+    forced = _plan(max_blocks_per_seq=mb, block_size=bs, partition_size=-2)
+    assert forced["range_tokens"] == 0 and forced["uses_reduce"]
 
 
 def test_plan_large_head_groups_split_into_sixteen():
@@ -107,7 +120,7 @@ def test_plan_large_head_groups_split_into_sixteen():
     (dict(num_seqs=16384), 4),
     (dict(max_blocks_per_seq=0), 3),
     (dict(partition_size=24), 3),
-    (dict(partition_size=-2), 3),
+    (dict(partition_size=-3), 3),
 ])
 def test_plan_rejects_bad_sizes(kw, code):
     with pytest.raises(pa.PagedAttnError) as ei:

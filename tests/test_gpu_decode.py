@@ -86,7 +86,7 @@ def test_full_config_store_bit_exact_and_decode_parity(cuda, name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("psize", [-1, 0, 16, 48, 512])
+@pytest.mark.parametrize("psize", [-2, -1, 0, 16, 48, 512])
 @pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"])
 def test_launch_modes_agree_with_oracle(cuda, name, psize):
     _say(f"[gpu] modes {name} partition_size={psize}")
@@ -111,7 +111,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("psize", [-1, 0, 16, 64])
+@pytest.mark.parametrize("psize", [-2, -1, 0, 16, 64])
 def test_small_shapes_and_edges(cuda, case, psize):
     dt, b, hq, hkv, d, bs, lens = CASES[case]
     _say(f"[gpu] small case {CASES[case]} partition_size={psize}")
@@ -132,7 +132,7 @@ def test_length_one_returns_value_row_exactly(cuda):
     import paged_attention_decode_amd as pa
     x = make_inputs(custom_config(dtype="bf16", batch=4, hq=8, hkv=2, lens=(1, 1, 1, 1), seed=3))
     dev = to_device(x, cuda)
-    for psize in (-1, 0):
+    for psize in (-2, -1, 0):
         out = _run_step(dev, x, partition_size=psize).cpu().numpy()
         k2, v2, _ = oracle_after_store(x)
         geo = geometry(x)
@@ -167,7 +167,7 @@ def test_poisoned_tail_slots_and_unused_blocks_change_nothing(cuda):
     x = make_inputs(cfg)
     x.slot_mapping[:] = -1
     geo = geometry(x)
-    clean = {p: _run_step(to_device(x, cuda), x, partition_size=p).cpu().numpy() for p in (-1, 0, 16)}
+    clean = {p: _run_step(to_device(x, cuda), x, partition_size=p).cpu().numpy() for p in (-2, -1, 0, 16)}
     kp = poison_blocks(x.k_cache, x.unused_blocks, cfg)
     vp = poison_blocks(x.v_cache, x.unused_blocks, cfg)
     # tail slots of each sequence's last block, written with NaN rows by the oracle's scatter
@@ -259,19 +259,22 @@ def test_caller_workspace_and_events(cuda):
     x = _inputs("qwen3_0p6b_bf16")
     c = x.cfg
     dev = to_device(x, cuda)
+    # balanced ranges: the mode with a workspace (automatic takes one pass for this batch)
     need = pa.workspace_bytes(c.batch, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size,
-                              c.max_blocks_per_seq, pa.DTYPE_BF16, 0)
+                              c.max_blocks_per_seq, pa.DTYPE_BF16, -2)
+    assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device=cuda)
     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     out = pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                                    dev["context_lens"], x.scale, out_dtype=torch.float32, workspace=ws, events=ev)
+                                    dev["context_lens"], x.scale, out_dtype=torch.float32, workspace=ws, events=ev,
+                                    partition_size=-2)
     torch.cuda.synchronize()
     assert ev[0].elapsed_time(ev[1]) > 0
     ref = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, x.scale, geometry(x))
     assert np.abs(out.cpu().numpy() - ref).max() <= 2e-3
     with pytest.raises(pa.PagedAttnError) as ei:
         pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                                  dev["context_lens"], x.scale, workspace=ws[:need // 2])
+                                  dev["context_lens"], x.scale, workspace=ws[:need // 2], partition_size=-2)
     assert ei.value.code == 5
 
 
@@ -340,7 +343,7 @@ def _fused_vs_two_calls(cuda, x, psize, out_dtype=None):
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("psize", [-1, 0, 16])
+@pytest.mark.parametrize("psize", [-2, -1, 0, 16])
 def test_fused_step_equals_store_then_decode(cuda, case, psize):
     dt, b, hq, hkv, d, bs, lens = CASES[case]
     _say(f"[gpu] fused step {CASES[case]} partition_size={psize}")
