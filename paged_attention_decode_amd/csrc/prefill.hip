@@ -468,12 +468,16 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
 // quarter of the K/V traffic from L2 of the per-wavefront kernel, which at head_dim 128 is
 // bound by exactly that traffic.
 //
-// LDS buffer of one step (T = one 16-key tile of K or V, 16 * D * 2 bytes):
-//   [0, T)     K tile A, as 16-byte operand chunks in lane order: (j * 64 + lane) * 16
-//   [T, 2T)    K tile B, the same
-//   [2T, 4T)   V: 16-byte slots (kq * D + d): bytes 0-7 = keys 4kq .. 4kq+3 of dim d in tile A,
-//              bytes 8-15 the same in tile B. Lane (kq, ln) reads the second product's operands
-//              for dims 32w + ln and 32w + 16 + ln as slots (kq * D + 32w + ln) and (... + 16).
+// LDS buffer of one step (T = one 16-key tile of K or V, 16 * D * 2 bytes), each tile stored
+// by its loader as 16-byte chunks in lane order, (j * 64 + lane) * 16 (contiguous, no bank
+// conflicts):
+//   [0, T)     K tile A: chunk j of lane (kq, ln) = key chunk 4j + kq of token ln, which is
+//              exactly the first product's operand, read back by the same lane
+//   [T, 2T)    K tile B
+//   [2T, 3T)   V tile A: chunk j of lane (kq, ln) = keys 4kq .. 4kq+3 of dims 32j + 2ln, +1
+//   [3T, 4T)   V tile B
+// The second product's operand for dim 32w + e (e < 32) and lane group kq is 8 bytes of each V
+// tile, at chunk (w, kq, e / 2), half e % 2; lanes ln = 0..15 read 128 contiguous bytes.
 template <int DT, int D>
 struct SharedCfg {
   using C = Cfg<DT, D>;
@@ -582,10 +586,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
   };
   // Values of keys at or beyond L may be anything: zero them before they are shared.
   auto store_share = [&](int st, char* buf) {
-    if (share_k) {
-#pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) *reinterpret_cast<u4*>(buf + half * T + (j * 64 + lane) * 16) = stg[j];
-    } else {
+    if (!share_k) {
       const int t0 = share_tile(st) * kTile;
       if (t0 + kTile > L) {
         const bool v0 = t0 + 4 * kq + 0 < L, v1 = t0 + 4 * kq + 1 < L;
@@ -595,14 +596,12 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
 #pragma unroll
         for (int j = 0; j < C::kLoads; ++j) stg[j] &= u4{m01, m23, m01, m23};
       }
-#pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) {
-        char* v = buf + 2 * T + (kq * D + 32 * j + 2 * ln) * 16 + half * 8;
-        *reinterpret_cast<u2*>(v) = u2{stg[j].x, stg[j].y};
-        *reinterpret_cast<u2*>(v + 16) = u2{stg[j].z, stg[j].w};
-      }
     }
+    char* dst = buf + wv * T + lane * 16;
+#pragma unroll
+    for (int j = 0; j < C::kLoads; ++j) *reinterpret_cast<u4*>(dst + j * 1024) = stg[j];
   };
+
 
   int raw_next = bt_entry(1);
   load_share(0, bt_entry(0));
@@ -643,11 +642,16 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
           }
         }
       }
+      // V^T operands: dims 32w + ln (va0) and 32w + 16 + ln (va1), keys of tile A then tile B.
       u4 va0[C::kLoads], va1[C::kLoads];
+      const int vo = (kq * 16 + (ln >> 1)) * 16 + (ln & 1) * 8;
 #pragma unroll
       for (int w = 0; w < C::kLoads; ++w) {
-        va0[w] = *reinterpret_cast<const u4*>(buf + 2 * T + (kq * D + 32 * w + ln) * 16);
-        va1[w] = *reinterpret_cast<const u4*>(buf + 2 * T + (kq * D + 32 * w + 16 + ln) * 16);
+        const char* va = buf + 2 * T + w * 1024 + vo;
+        const u2 a0 = *reinterpret_cast<const u2*>(va), b0 = *reinterpret_cast<const u2*>(va + T);
+        const u2 a1 = *reinterpret_cast<const u2*>(va + 128), b1 = *reinterpret_cast<const u2*>(va + T + 128);
+        va0[w] = u4{a0[0], a0[1], b0[0], b0[1]};
+        va1[w] = u4{a1[0], a1[1], b1[0], b1[1]};
       }
       const bool open = t0 + 2 * kTile - 1 <= p_first;
 #pragma unroll
@@ -797,7 +801,7 @@ int prefill_queries_per_item(int dtype, int head_dim, int gh_max) {
 }
 
 size_t prefill_shared_buffer_bytes(int head_dim) {
-  return 2 * 4 * (size_t)kTile * head_dim * 2;
+  return head_dim == 128 ? 2 * (size_t)SharedCfg<kBF16, 128>::kBufBytes : 0;
 }
 
 hipError_t launch_prefill_shared(const PrefillArgs& a, int dtype, int head_dim, int grid, size_t lds,
