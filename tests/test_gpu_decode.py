@@ -107,6 +107,7 @@ CASES = [
     ("bf16", 4, 16, 2, 256, 256, (300, 256, 257, 1)),
     ("fp32", 2, 8, 1, 64, 128, (129, 300)),
     ("bf16", 6, 8, 8, 128, 16, (0, 5, 0, 64, 3, 1)),   # empty contexts give zeros
+    ("fp32", 2, 4, 2, 256, 16, (40, 77)),              # fp32 at head_dim 256 (largest register set)
 ]
 
 
