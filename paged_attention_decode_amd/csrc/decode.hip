@@ -215,7 +215,7 @@ struct Piece {
         const float alpha = exp2_fast(m - m_new);
         float p[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) p[rr] = exp2_fast(z[rr] - m_new);
+        for (int rr = 0; rr < 4; ++rr) p[rr] = exp2_fast(z[rr] - (m_new - weight_log2_scale<DT>(0)));
         l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
         m = m_new;
 #pragma unroll

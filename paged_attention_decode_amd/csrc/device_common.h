@@ -51,6 +51,17 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// fp16 inputs: the softmax weights are computed times 2^kF16WeightLog2 (the same factor in the
+// running sum, so nothing else changes), which keeps them in fp16's normal range when they are
+// split into value + remainder for the second product. Unscaled, a weight below 2^-14 of the
+// running maximum would be an fp16 subnormal, with absolute precision 2^-25 only, and many such
+// weights could add up to a visible error. Decode weights are at most 1 before scaling
+// (2^15 after); prefill allows 2^8 (lazy rescale) and scales by 2^7.
+template <int DT>
+constexpr float weight_log2_scale(int max_weight_log2) {
+  return DT == kF16 ? (float)(15 - max_weight_log2) : 0.0f;
+}
+
 // Maximum over lanes l, l^16, l^32 and l^48 (the four 16-lane rows), with gfx950's row-swap
 // instructions: each swap leaves lane l's value and its partner's in the two results.
 // The maxima are IEEE-2019 `maximum` (gfx950 has it natively, with a three-input form): unlike

@@ -290,7 +290,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
       const float alpha = exp2_fast(m[ct] - m_use);
       float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, -m_use));
+      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, weight_log2_scale<DT>(8) - m_use));
       l[ct] = fmaf(l[ct], alpha, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
       m[ct] = m_use;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
@@ -676,7 +676,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
         const float alpha = exp2_fast(m[ct] - m_use);
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, -m_use));
+        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, weight_log2_scale<DT>(8) - m_use));
         l[ct] = fmaf(l[ct], alpha, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
         m[ct] = m_use;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {

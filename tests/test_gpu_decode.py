@@ -362,3 +362,52 @@ def test_fused_step_full_configs(cuda, name, psize):
     _say(f"[gpu] fused step full config {name} partition_size={psize}")
     x = _inputs(name)
     _fused_vs_two_calls(cuda, x, psize)
+
+
+def _tiny_weight_case(length=16384, d=64, bs=16):
+    """fp16, one sequence, G = 1: key 0 dominates and every other key has weight ~2^-15 of it, all
+    with the same value sign, so rounding errors on the small weights add up in one direction.
+    Built with the oracle's own scatter on a shuffled block table."""
+    geo = oracle.CacheGeometry(num_blocks=length // bs + 8, num_kv_heads=1, head_dim=d, block_size=bs, dtype="fp16")
+    rng = np.random.default_rng(2024)
+    q = np.zeros((1, 1, d), np.float16)
+    q[0, 0, 0] = 8.0
+    k = np.zeros((length, 1, d), np.float16)
+    k[0, 0, 0] = 10.3984375                 # scale 1/8: logit gap 10.398 = 15.0 in log2 units
+    v = np.full((length, 1, d), 4.0, np.float16)
+    v[0] = -4.0
+    v[1:, 0, :] += rng.integers(0, 8, (length - 1, d)).astype(np.float16) * np.float16(0.125)
+    blocks = rng.permutation(geo.num_blocks)[:length // bs].astype(np.int32)
+    slots = (blocks[np.arange(length) // bs] * bs + np.arange(length) % bs).astype(np.int32)
+    kc = np.zeros(int(np.prod(geo.k_shape)), np.float16)
+    vc = np.zeros(int(np.prod(geo.v_shape)), np.float16)
+    kc, vc = oracle.store_kvcache(k, v, slots, kc, vc, geo)
+    return geo, q, kc, vc, blocks[None, :], np.array([length], np.int32)
+
+
+def test_fp16_many_tiny_weights_keep_their_precision(cuda):
+    """Without scaling, each 2^-15 weight would be an fp16 subnormal with absolute precision 2^-25
+    in its value + remainder pair, and 16383 aligned rounding errors reach about 1e-3 (measured
+    1.08e-3 in one pass). With scaling what remains is fp32 accumulation: one wavefront adding
+    16383 equal terms (one pass) measures about 5e-5, split ranges about 4e-6. The bound 2e-4
+    separates the two by a factor of 20."""
+    import torch
+    import paged_attention_decode_amd as pa
+    geo, q, kc, vc, bt, cl = _tiny_weight_case()
+    ref = oracle.decode(q, kc, vc, bt, cl, 0.125, geo)
+    dev = dict(q=torch.from_numpy(q).to(cuda),
+               k=torch.from_numpy(kc).view(geo.k_shape).to(cuda), v=torch.from_numpy(vc).view(geo.v_shape).to(cuda),
+               bt=torch.from_numpy(bt).to(cuda), cl=torch.from_numpy(cl).to(cuda))
+    for psize in (-2, -1, 0, 512):
+        out = pa.paged_attention_decode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"], 0.125,
+                                        out_dtype=torch.float32, partition_size=psize)
+        torch.cuda.synchronize()
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        _say(f"[gpu] tiny fp16 weights, partition_size={psize}: max-abs error {err:.2e}")
+        assert err <= 2e-4, psize
+    pre = pa.paged_prefill(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"],
+                           torch.tensor([0, 1], dtype=torch.int32, device=cuda), 0.125, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = float(np.abs(pre.cpu().numpy() - ref[0]).max())
+    _say(f"[gpu] tiny fp16 weights, one-token prefill: max-abs error {err:.2e}")
+    assert err <= 2e-4
