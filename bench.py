@@ -44,8 +44,8 @@ COPY_BYTES = 256 << 20
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--partition-size", type=int, default=0,
                     help="0 automatic, -1 one pass, -2 balanced split, >0 fixed ranges of that many tokens")
@@ -75,6 +75,53 @@ def parse():
                          "--stats run of this script, then exit")
     ap.add_argument("--trace-command", default="", help="the profiling command, recorded in the summary")
     return ap.parse_args()
+
+
+class TimingEvent:
+    """A HIP event for timing only, recorded without the system-scope fence.
+
+    torch.cuda.Event's default HIP event writes back and invalidates the caches when it is
+    recorded, which on MI355X adds about 11 us to a 240 us decode step and slows the work after
+    it. hipEventDisableSystemFence drops that fence; the HIP headers name timing as its use.
+    Elapsed times are read only after a device synchronisation. Same interface as the
+    torch.cuda.Event calls used here: record(stream), elapsed_time(end), cuda_event.
+    """
+    _hip = None
+    _DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        handle = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(handle), self._DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = handle.value
+
+    def record(self, stream=None):
+        import torch
+        s = torch.cuda.current_stream() if stream is None else stream
+        rc = TimingEvent._hip.hipEventRecord(self.cuda_event, s.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, end.cuda_event)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
+            TimingEvent._hip.hipEventDestroy(self.cuda_event)
 
 
 def kernel_source_sha(kernel: str = "decode") -> str:
@@ -269,7 +316,7 @@ def extra_timings(calls: dict, reps: int, stream_bytes: int, dev) -> dict:
     for name, fn in calls.items():
         fn()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
         for b, e in evs:
             b.record()
             fn()
@@ -279,7 +326,7 @@ def extra_timings(calls: dict, reps: int, stream_bytes: int, dev) -> dict:
     buf = torch.ones(stream_bytes // 4, dtype=torch.float32, device=dev)
     buf.sum()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(5)]
     for b, e in evs:
         b.record()
         buf.sum()
@@ -326,7 +373,7 @@ def prefill_bench(args) -> None:
     for _ in range(max(1, args.warmup)):
         pa.paged_prefill(q, k_cache, v_cache, bt, cl, qst, x.scale, out)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     t0 = time.perf_counter()
     ev[0].record()
     for _ in range(args.steps):
@@ -421,7 +468,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    events = [(TimingEvent(), TimingEvent())
               for _ in range(args.steps)]
     for e in events:  # materialise the HIP events outside the timed region
         e[0].record(stream)
@@ -469,7 +516,7 @@ def main():
         scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         for _ in range(args.cold_steps):
             scratch.sum()
-            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev = (TimingEvent(), TimingEvent())
             step(ev)
             torch.cuda.synchronize()
             cold.append(ev[0].elapsed_time(ev[1]))
