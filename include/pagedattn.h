@@ -254,7 +254,10 @@ int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t 
  *   q            [num_tokens][num_heads][head_dim], heads and dims contiguous,
  *                tokens q_token_stride ELEMENTS apart.
  *   query_start  [num_seqs + 1] int32, non-decreasing, query_start[num_seqs]
- *                <= num_tokens.
+ *                <= num_tokens. Being device memory it is not checked: values
+ *                are clamped into [0, num_tokens] (and each sequence's end to
+ *                at least its start), so malformed content gives meaningless
+ *                rows but never a q read or out write outside the buffers.
  *   out          [num_tokens][num_heads][head_dim] contiguous, fp32 or dtype.
  *   Other arguments and limits as for pa_paged_attention_decode.
  */

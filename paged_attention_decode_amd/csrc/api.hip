@@ -274,6 +274,7 @@ int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start = query_start;
+  a.num_tokens = num_tokens;
   a.out = out;
   a.q_token_stride = q_token_stride;
   a.num_blocks = num_blocks;

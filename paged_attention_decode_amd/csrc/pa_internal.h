@@ -86,6 +86,7 @@ struct PrefillArgs {
   int64_t num_blocks;
   float scale_log2;
   int32_t num_seqs;
+  int32_t num_tokens;           // rows of q and out
   int32_t num_heads;
   int32_t num_kv_heads;
   int32_t group;

@@ -61,6 +61,21 @@ struct PrefillCfg {
 };
 
 
+// Sequence s's context length L and its new query rows q0 .. q0+n-1, with every value read
+// from device memory clamped into what the call describes: L into [0, max_len], the rows into
+// [0, num_tokens) and n into [0, L]. No query_start or context_lens content can move a q read or
+// an out write outside the buffers.
+__device__ __forceinline__ void seq_rows(const PrefillArgs& a, int s, int& L, int& q0, int& n) {
+  const int max_len = a.max_blocks << a.bs_log2;
+  L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > max_len ? max_len : L);
+  int b = a.query_start[s], e = a.query_start[s + 1];
+  b = b < 0 ? 0 : (b > a.num_tokens ? a.num_tokens : b);
+  e = e < b ? b : (e > a.num_tokens ? a.num_tokens : e);
+  q0 = b;
+  n = e - b < L ? e - b : L;
+}
+
 template <int DT, int D>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g, int hg, int qb, int lane) {
   using C = Cfg<DT, D>;
@@ -68,12 +83,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   const int kq = lane >> 4;
   const int ln = lane & 15;
   const int bs = a.block_size;
-  const int max_len = a.max_blocks << a.bs_log2;
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > max_len ? max_len : L);
-  const int q0 = a.query_start[s];
-  int n = a.query_start[s + 1] - q0;
-  n = n < 0 ? 0 : (n > L ? L : n);
+  int L, q0, n;
+  seq_rows(a, s, L, q0, n);
   const int gh = a.gh_max;            // columns per query (heads of one group)
   const int qpt = kHeadsPerTile / gh; // queries per column tile
   const int qb_queries = NC * qpt;
@@ -391,17 +402,14 @@ __device__ __forceinline__ int xcd_group() {
 __device__ int build_item_prefix(const PrefillArgs& a, int queries_per_item, int32_t* s_prefix, int32_t* s_wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int max_len = a.max_blocks << a.bs_log2;
   const int H = a.num_kv_heads * a.n_hg;
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += kDecodeThreads) {
     const int i = base + tid;
     int v = 0;
     if (i < a.num_seqs) {
-      int L = a.context_lens[i];
-      L = L < 0 ? 0 : (L > max_len ? max_len : L);
-      int n = a.query_start[i + 1] - a.query_start[i];
-      n = n < 0 ? 0 : (n > L ? L : n);
+      int L, q0, n;
+      seq_rows(a, i, L, q0, n);
       v = ((n + queries_per_item - 1) / queries_per_item) * H;
     }
     int x = v;
@@ -497,12 +505,8 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
   const int kq = lane >> 4;
   const int ln = lane & 15;
   const int bs = a.block_size;
-  const int max_len = a.max_blocks << a.bs_log2;
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > max_len ? max_len : L);
-  const int q0 = a.query_start[s];
-  int n = a.query_start[s + 1] - q0;
-  n = n < 0 ? 0 : (n > L ? L : n);
+  int L, q0, n;
+  seq_rows(a, s, L, q0, n);
   const int gh = a.gh_max;
   const int qpt = kHeadsPerTile / gh;
   const int qb_queries = NC * qpt;

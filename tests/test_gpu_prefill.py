@@ -123,3 +123,36 @@ def test_prefill_of_many_sequences_uses_the_per_wavefront_kernel(cuda):
     for s_ in seqs:
         rows = slice(qs[s_], qs[s_ + 1])
         assert np.abs(out[rows] - ref[rows]).max() <= TOL["bf16"], s_
+
+
+def test_malformed_query_start_stays_inside_the_buffers(cuda):
+    """query_start lives on the device and is not checked on the host: starts past num_tokens,
+    negative starts and decreasing ends are clamped, so q and out outside the described rows are
+    never touched. Rows of well-formed sequences are still correct."""
+    import torch
+    import paged_attention_decode_amd as pa
+    x = make_inputs(custom_config(dtype="bf16", batch=4, hq=8, hkv=2, d=128, bs=16, lens=(40, 60, 30, 50), seed=91))
+    dev = to_device(x, cuda)
+    num_tokens = 70
+    # seq 0 starts at -5 (clamped to 0), seq 1 ends past num_tokens (clamped to 70), seq 2 starts
+    # past num_tokens, seq 3 ends before it starts: after clamping, seqs 0 and 1 own rows 0..39
+    # and 40..69, seqs 2 and 3 none
+    qs = np.array([-5, 40, 1000, 70, 30], np.int32)
+    rng = np.random.default_rng(91)
+    q_host = to_storage(rng.standard_normal((num_tokens, 8, 128), dtype=np.float32), "bf16")
+    # guard rows on both sides of q and out: a read or write outside [guard, guard + num_tokens)
+    # would show there
+    guard = 64
+    q_big = torch.zeros((num_tokens + 2 * guard, 8, 128), dtype=torch.bfloat16, device=cuda)
+    q_big[guard:guard + num_tokens] = np_to_torch(q_host, "bf16").to(cuda)
+    out_big = torch.full((num_tokens + 2 * guard, 8, 128), 7.0, dtype=torch.float32, device=cuda)
+    pa.paged_prefill(q_big[guard:guard + num_tokens], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                     dev["context_lens"], torch.from_numpy(qs).to(cuda), x.scale,
+                     out=out_big[guard:guard + num_tokens])
+    torch.cuda.synchronize()
+    ob = out_big.cpu().numpy()
+    assert (ob[:guard] == 7.0).all() and (ob[guard + num_tokens:] == 7.0).all()
+    # the clamped rows are the last 40 and 30 queries of sequences 0 and 1
+    ref = oracle.prefill(q_host, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
+                         np.array([0, 40, 70, 70, 70], np.int32), x.scale, geometry(x), seqs=[0, 1])
+    assert np.abs(ob[guard:guard + num_tokens] - ref).max() <= TOL["bf16"]
