@@ -550,11 +550,22 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   auto row_of = [&](int p) -> int64_t {
     return ((int64_t)(wa + p) * 2 + (p == 0 ? slot_a : 0)) * a.gh_max + n;
   };
-  float M = -INFINITY;
-  for (int p0 = 0; p0 < np; p0 += 64) {
-    const int p = p0 + lane;
-    if (p < np) M = fmaxf(M, a.ws_lse[row_of(p)]);
-  }
+  // Pieces 0..63's lse and the first kBatch pieces' rows are loaded together: the rows do not
+  // depend on the weights, so the merge waits for memory once before its first products.
+  float vals[kBatch][kPer];
+  auto load_batch = [&](int first, int last) {
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const float* o = a.ws_o + row_of(min(first + b, last)) * D + lane * kPer;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) vals[b][j] = o[j];
+    }
+  };
+  const float x_raw = a.ws_lse[row_of(min(lane, np - 1))];
+  const float x0 = lane < np ? x_raw : -INFINITY;
+  load_batch(0, np - 1);
+  float M = x0;
+  for (int p = 64 + lane; p < np; p += 64) M = fmaxf(M, a.ws_lse[row_of(p)]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
@@ -564,24 +575,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   float wsum = 0.f;
   for (int p0 = 0; p0 < np; p0 += 64) {
     const int p = p0 + lane;
-    float wl = 0.f;
-    if (p < np) {
-      const float x = a.ws_lse[row_of(p)];
-      wl = (x == -INFINITY) ? 0.f : exp2_fast(x - M);
-    }
+    const float x = p0 == 0 ? x0 : (p < np ? a.ws_lse[row_of(p)] : -INFINITY);
+    const float wl = (x == -INFINITY) ? 0.f : exp2_fast(x - M);
     wsum += wl;
     const int cnt = min(64, np - p0);
     for (int k0 = 0; k0 < cnt; k0 += kBatch) {
-      float vals[kBatch][kPer];
+      if (p0 + k0 != 0) load_batch(p0 + k0, p0 + cnt - 1);
       float wk[kBatch];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int k = min(k0 + b, cnt - 1);
-        wk[b] = (k0 + b < cnt) ? __shfl(wl, k) : 0.f;
-        const float* o = a.ws_o + row_of(p0 + k) * D + lane * kPer;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) vals[b][j] = o[j];
-      }
+      for (int b = 0; b < kBatch; ++b) wk[b] = (k0 + b < cnt) ? __shfl(wl, min(k0 + b, cnt - 1)) : 0.f;
 #pragma unroll
       for (int b = 0; b < kBatch; ++b)
 #pragma unroll
