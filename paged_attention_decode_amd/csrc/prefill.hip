@@ -275,39 +275,64 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     // every key of the step visible to every column: no masking
     const bool open = t0 + 2 * kTile - 1 <= p_first;
 
+    // Both wave-uniform branches of the step (the causal mask, the rescale) are taken once for
+    // all column tiles. The exponentials, weight splits and second products of all tiles then
+    // form one branch-free block, in which the compiler can interleave one tile's products with
+    // the next tile's softmax.
+    float x[NC][8];
 #pragma unroll
-    for (int ct = 0; ct < NC; ++ct) {
-      float x[8];
+    for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        x[r] = sA[ct][r];
-        x[4 + r] = sB[ct][r];
+        x[ct][r] = sA[ct][r];
+        x[ct][4 + r] = sB[ct][r];
       }
-      if (!open) {
+    if (!open) {
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = t0 + (j < 4 ? 0 : kTile) + 4 * kq + (j & 3);
-          if (t > pos[ct]) x[j] = -INFINITY;
+          if (t > pos[ct]) x[ct][j] = -INFINITY;
         }
-      }
+    }
+    float m_use[NC], alpha[NC];
+    bool moved = false;
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
       // IEEE-2019 maximum: gfx950 has a three-input form, and it needs no NaN quieting first.
-      float mt = fmax8(x);
-      mt = max_over_rows(mt);
+      const float mt = max_over_rows(fmax8(x[ct]));
       // Key 0 is visible to every column, so m is finite from the first step on. The running
       // maximum is kept unless it grew by more than 8 (log2 units): weights stay below 2^8,
       // and the accumulators are rescaled only on such jumps instead of on every new maximum.
       const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
-      const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
-      const float alpha = exp2_fast(m[ct] - m_use);
+      m_use[ct] = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
+      alpha[ct] = exp2_fast(m[ct] - m_use[ct]);
+      moved = moved || alpha[ct] != 1.0f;
+    }
+    if constexpr (DT == kBF16 && NC > 2) {
+      // One rescale branch per tile here: with a single branch for all four tiles this instance
+      // needs more than 256 VGPRs (two wavefronts per SIMD no longer fit).
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
+        if (__builtin_amdgcn_ballot_w64(alpha[ct] != 1.0f) != 0) {
+#pragma unroll
+          for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
+        }
+    } else if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+        for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
+    }
+
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
       float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, weight_log2_scale<DT>(8) - m_use));
-      l[ct] = fmaf(l[ct], alpha, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-      m[ct] = m_use;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha;
-      }
+      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m_use[ct]));
+      l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      m[ct] = m_use[ct];
 
       if constexpr (DT == kF32) {
 #pragma unroll
@@ -658,35 +683,48 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
         va1[w] = u4{a1[0], a1[1], b1[0], b1[1]};
       }
       const bool open = t0 + 2 * kTile - 1 <= p_first;
+      // One causal-mask branch and one rescale branch for all column tiles, as in prefill_item.
+      float x[NC][8];
 #pragma unroll
-      for (int ct = 0; ct < NC; ++ct) {
-        float x[8];
+      for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          x[r] = sA[ct][r];
-          x[4 + r] = sB[ct][r];
+          x[ct][r] = sA[ct][r];
+          x[ct][4 + r] = sB[ct][r];
         }
-        if (!open) {
+      if (!open) {
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int t = t0 + (j < 4 ? 0 : kTile) + 4 * kq + (j & 3);
-            if (t > pos[ct]) x[j] = -INFINITY;
+            if (t > pos[ct]) x[ct][j] = -INFINITY;
           }
-        }
-        const float mt = max_over_rows(fmax8(x));
+      }
+      float m_use[NC], alpha[NC];
+      bool moved = false;
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const float mt = max_over_rows(fmax8(x[ct]));
         // Key 0 is visible to every column; the running maximum moves only on jumps above 8.
         const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
-        const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
-        const float alpha = exp2_fast(m[ct] - m_use);
+        m_use[ct] = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
+        alpha[ct] = exp2_fast(m[ct] - m_use[ct]);
+        moved = moved || alpha[ct] != 1.0f;
+      }
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+          for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
+      }
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[j], c, weight_log2_scale<DT>(8) - m_use));
-        l[ct] = fmaf(l[ct], alpha, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-        m[ct] = m_use;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-          for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha;
-        }
+        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m_use[ct]));
+        l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        m[ct] = m_use[ct];
         u4 ph, pl;
         if constexpr (DT == kBF16) {
 #pragma unroll
