@@ -170,6 +170,13 @@ int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_
  *       kv head) contexts are divided evenly over the wavefronts the device
  *       holds at once, so long and short sequences finish together; contexts
  *       cut by a range boundary are merged by the reduce kernel.
+ *   -3  workgroup split: each (sequence, kv head) context is handled by one
+ *       workgroup, whose four wavefronts stream equal shares of its tiles at
+ *       once and merge their partial results in LDS (same log-sum-exp merge as
+ *       the reduce kernel); no workspace and no reduce kernel. Shortens the
+ *       per-context chain of small batches. Where the four partial rows would
+ *       exceed 64 KiB of LDS (head_dim 256 with 16 query heads per kv head) it
+ *       runs as one pass.
  *   >0  fixed ranges of partition_size tokens (a multiple of 16) over the same
  *       concatenated tile stream. The device's resident wavefronts loop over
  *       the ranges; the workspace has rows for the ranges of the longest
@@ -272,7 +279,7 @@ int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache,
  * num_cus > 0 (num_cus <= 0 queries the current device). Fills any non-NULL
  * output: the wavefront count of the attention kernel; range_tokens, the
  * tokens per wavefront range (> 0 fixed, 0 balanced over the data, -1 one
- * pass); whether the reduce kernel runs; and the workspace bytes the call
+ * pass, -3 workgroup split); whether the reduce kernel runs; and the workspace bytes the call
  * needs. Returns the pa_status the decode call would return for these sizes.
  */
 int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

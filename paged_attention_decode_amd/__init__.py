@@ -236,7 +236,8 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
 
     partition_size: 0 automatic (default: one pass when max_blocks_per_seq *
     block_size <= 512, else balanced split), -1 one pass per sequence, -2
-    balanced split, >0 fixed ranges of that many tokens. cached_prefix_tokens: leading tokens
+    balanced split, -3 workgroup split (four wavefronts per (sequence, kv head),
+    merged in LDS), >0 fixed ranges of that many tokens. cached_prefix_tokens: leading tokens
     of each context read with cached loads, the rest streamed (0 library
     default, -1 stream all; speed only). workspace: optional uint8 CUDA tensor
     (see ``workspace_bytes``). events: optional (begin, end) torch.cuda.Event

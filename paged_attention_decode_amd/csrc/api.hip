@@ -43,7 +43,8 @@ constexpr int kGroupsPerCU = PA_GROUPS_PER_CU;
 #define PA_PREFILL_SHARED 1
 #endif
 constexpr bool kPrefillShared = PA_PREFILL_SHARED != 0;
-// partition_size values: 0 automatic, -1 one pass, -2 balanced ranges, > 0 fixed ranges.
+// partition_size values: 0 automatic, -1 one pass, -2 balanced ranges, -3 workgroup split,
+// > 0 fixed ranges.
 constexpr int kBalanced = -2;
 constexpr int64_t kOnePassMaxTokens = 512;
 
@@ -71,7 +72,7 @@ struct Plan {
   int64_t num_waves = 0;
   int64_t num_ranges = 0;  // ranges the workspace has rows for (split modes)
   int grid = 0;
-  int range_tiles = 0;  // -1 one pass, 0 balanced, >0 fixed
+  int range_tiles = 0;  // -1 one pass, kWorkgroupSplit, 0 balanced, >0 fixed
   bool reduce = false;
   size_t lds = 0;
   int n_hg = 0, gh_max = 0, segs_per_seq = 0;
@@ -98,8 +99,8 @@ int check_decode_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   if (max_blocks <= 0) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d must be positive", max_blocks);
   if ((int64_t)max_blocks * block_size > INT32_MAX / 2)
     return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size too large");
-  if (partition_size < -2 || (partition_size > 0 && partition_size % kTile != 0))
-    return fail(PA_ERR_SHAPE, "partition_size %d must be -2, -1, 0 or a positive multiple of 16", partition_size);
+  if (partition_size < kWorkgroupSplit || (partition_size > 0 && partition_size % kTile != 0))
+    return fail(PA_ERR_SHAPE, "partition_size %d must be -3, -2, -1, 0 or a positive multiple of 16", partition_size);
   return PA_OK;
 }
 
@@ -120,7 +121,18 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
   // runs. Otherwise balanced ranges.
   if (partition_size == 0)
     partition_size = (int64_t)max_blocks * block_size <= kOnePassMaxTokens ? -1 : kBalanced;
-  if (partition_size == -1) {
+  // Workgroup split keeps four partial outputs and their log-sum-exps in LDS; where they would
+  // not fit in 64 KiB (head_dim 256 with 16 heads per group) it runs as one pass.
+  const size_t split_lds = (size_t)kWavesPerGroup * p->gh_max * (head_dim + 1) * sizeof(float);
+  if (partition_size == kWorkgroupSplit && split_lds > 65536) partition_size = -1;
+  if (partition_size == kWorkgroupSplit) {
+    // One workgroup per segment (persistent when there are more segments than resident groups).
+    p->range_tiles = kWorkgroupSplit;
+    const int64_t groups = resident / kWavesPerGroup;
+    waves = (segs < groups ? segs : groups) * kWavesPerGroup;
+    p->lds = split_lds;
+    p->reduce = false;
+  } else if (partition_size == -1) {
     p->range_tiles = -1;
     waves = segs < resident ? segs : resident;
     p->lds = 0;

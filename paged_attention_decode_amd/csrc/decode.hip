@@ -46,9 +46,11 @@ struct Piece {
 
   // Runs tiles [lt0, lt1) of segment (s, r). complete: the piece is the whole
   // segment, so the normalised result goes straight to `out`; otherwise to
+  // part_o / part_lse (rows of the group's heads, in LDS) when given, else to
   // workspace slot `slot` of range `rng`.
   static __device__ __forceinline__ void run(const DecodeArgs& a, int s, int r, int L, int lt0, int lt1,
-                                             bool complete, int rng, int slot, int lane) {
+                                             bool complete, int rng, int slot, int lane,
+                                             float* part_o = nullptr, float* part_lse = nullptr) {
     // All of these are the same in every lane. Saying so lets the compiler keep what derives
     // from them in scalar registers, and read the block table with scalar loads.
     s = __builtin_amdgcn_readfirstlane(s);
@@ -343,6 +345,11 @@ struct Piece {
     bool as_f32 = a.out_f32 != 0;
     if (complete) {
       base = ((int64_t)s * a.num_heads + h0 + ln) * D;
+    } else if (part_o != nullptr) {
+      dst = part_o;
+      base = (int64_t)ln * D;
+      as_f32 = true;
+      if (kq == 0) part_lse[ln] = m + __log2f(lt);
     } else {
       const int64_t row = ((int64_t)rng * 2 + slot) * a.gh_max + ln;
       dst_f32 = a.ws_o;
@@ -377,7 +384,9 @@ struct Piece {
 
 template <int DT, int D, bool FUSE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
-  extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]: first global tile of each sequence
+  // Split modes: [num_seqs + 1], the first global tile of each sequence. Workgroup split: the
+  // partial rows of the segment being merged.
+  extern __shared__ int32_t s_prefix[];
   __shared__ int32_t s_wsum[kWavesPerGroup];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -392,6 +401,67 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
 #endif
   const int max_len = a.max_blocks << a.bs_log2;
   const int H = a.segs_per_seq;
+
+  if (a.range_tiles == kWorkgroupSplit) {
+    // Workgroup split: a workgroup takes whole segments, and its wavefronts stream equal shares
+    // of the segment's tiles at once. Each share leaves its normalised partial output and
+    // log2-sum-exp2 in LDS, and the workgroup merges them there: no workspace, no second kernel.
+    // A one-tile segment is finished by wavefront 0 alone.
+    float* part_o = reinterpret_cast<float*>(s_prefix);            // [kWavesPerGroup][gh_max][D]
+    float* part_lse = part_o + kWavesPerGroup * a.gh_max * D;      // [kWavesPerGroup][gh_max]
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nseg = a.num_seqs * H;
+#if PA_XCD_REMAP
+    const int first = grp;
+#else
+    const int first = blockIdx.x;
+#endif
+    for (int seg = first; seg < nseg; seg += gridDim.x) {
+      const int s = seg / H;
+      const int r = seg - s * H;
+      const int L = clamp_len(a.context_lens[s], max_len);
+      const int tiles = max(1, (L + kTile - 1) / kTile);
+      const int parts = min(kWavesPerGroup, tiles);
+      if (parts == 1) {
+        if (wv == 0) Piece<DT, D, FUSE>::run(a, s, r, L, 0, tiles, true, 0, 0, lane);
+        continue;
+      }
+      // Every share is non-empty and starts below L, so every partial has a finite lse.
+      if (wv < parts)
+        Piece<DT, D, FUSE>::run(a, s, r, L, wv * tiles / parts, (wv + 1) * tiles / parts, false, 0, 0, lane,
+                                part_o + wv * a.gh_max * D, part_lse + wv * a.gh_max);
+      __syncthreads();
+      const int g = r / a.n_hg;
+      const int hg = r - g * a.n_hg;
+      const int h0 = g * a.group + hg * kHeadsPerTile;
+      const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
+      // out = sum_w 2^(lse_w - M) o_w / sum_w 2^(lse_w - M), M = max_w lse_w, shares in order.
+      for (int e = tid; e < gh * D; e += kDecodeThreads) {
+        const int h = e / D;
+        const int d = e - h * D;
+        float M = -INFINITY;
+        for (int w = 0; w < parts; ++w) M = fmaxf(M, part_lse[w * a.gh_max + h]);
+        float num = 0.f, den = 0.f;
+        for (int w = 0; w < parts; ++w) {
+          const float wt = exp2_fast(part_lse[w * a.gh_max + h] - M);
+          den += wt;
+          num += wt * part_o[(w * a.gh_max + h) * D + d];
+        }
+        const float v = num / den;
+        const int64_t o = ((int64_t)s * a.num_heads + h0 + h) * D + d;
+        if (a.out_f32) {
+          reinterpret_cast<float*>(a.out)[o] = v;
+        } else if constexpr (DT == kBF16) {
+          reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)bf16_bits_rne(v);
+        } else if constexpr (DT == kF16) {
+          reinterpret_cast<_Float16*>(a.out)[o] = (_Float16)v;
+        }
+      }
+      // The next segment's shares overwrite these rows.
+      __syncthreads();
+    }
+    return;
+  }
 
   if (a.range_tiles < 0) {
     // One pass: each wavefront takes whole segments.

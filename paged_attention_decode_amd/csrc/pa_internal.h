@@ -19,6 +19,9 @@ constexpr int kWavesPerGroup = kDecodeThreads / 64;
 constexpr int kHeadsPerTile = 16;
 // Largest batch: per-sequence tile prefix sums live in LDS (4 bytes each).
 constexpr int kMaxSeqs = 16383;
+// partition_size (and DecodeArgs::range_tiles) of the workgroup-split mode: the wavefronts of a
+// workgroup share one segment's tiles and merge their partial results in LDS.
+constexpr int kWorkgroupSplit = -3;
 // Balanced mode never gives a wavefront fewer tiles than this.
 #ifndef PA_MIN_TILES_PER_WAVE
 #define PA_MIN_TILES_PER_WAVE 2
@@ -50,7 +53,7 @@ struct DecodeArgs {
   int32_t max_blocks;     // block table row length
   int32_t out_f32;        // 1: fp32 output, 0: output in the input dtype
   int32_t num_waves;      // wavefronts launched
-  int32_t range_tiles;    // >0 fixed tiles per wavefront, 0 balanced, -1 one pass
+  int32_t range_tiles;    // >0 fixed tiles per wavefront, 0 balanced, -1 one pass, kWorkgroupSplit
   int32_t cached_prefix_tokens;  // tiles starting before this token use cached loads, later ones stream
   // Fused scatter of the step's token at position L-1 (null: plain decode).
   const void* k_new;      // [num_seqs][num_kv_heads][head_dim]

@@ -69,6 +69,24 @@ def test_plan_one_pass_needs_no_workspace():
     assert p["num_waves"] == 256 * 8  # one wavefront per (sequence, kv head), fewer than resident
 
 
+def test_plan_workgroup_split_uses_lds_not_a_workspace():
+    # one workgroup of four wavefronts per (sequence, kv head) segment, up to the resident groups
+    p = _plan(partition_size=-3)
+    assert p["range_tokens"] == -3 and not p["uses_reduce"] and p["workspace_bytes"] == 0
+    assert p["num_waves"] == 256 * 2 * 4  # 2048 segments, 512 resident workgroups
+    small = _plan(num_seqs=3, num_heads=4, num_kv_heads=2, head_dim=64, max_blocks_per_seq=4, partition_size=-3,
+                  dtype_code=pa.DTYPE_F32)
+    assert small["num_waves"] == 3 * 2 * 4
+
+
+def test_plan_workgroup_split_falls_back_where_lds_would_not_fit():
+    # four partial rows of 16 heads x 256 dims (plus lse) exceed 64 KiB: one pass instead
+    p = _plan(num_heads=32, num_kv_heads=2, head_dim=256, partition_size=-3)
+    assert p["range_tokens"] == -1 and not p["uses_reduce"]
+    q = _plan(num_heads=30, num_kv_heads=2, head_dim=256, partition_size=-3)
+    assert q["range_tokens"] == -3
+
+
 def test_plan_fixed_ranges_cover_the_upper_bound():
     p = _plan(num_seqs=4, num_heads=4, num_kv_heads=2, head_dim=64, max_blocks_per_seq=4, partition_size=32,
               dtype_code=pa.DTYPE_F32)
@@ -120,7 +138,7 @@ def test_plan_large_head_groups_split_into_sixteen():
     (dict(num_seqs=16384), 4),
     (dict(max_blocks_per_seq=0), 3),
     (dict(partition_size=24), 3),
-    (dict(partition_size=-3), 3),
+    (dict(partition_size=-4), 3),
 ])
 def test_plan_rejects_bad_sizes(kw, code):
     with pytest.raises(pa.PagedAttnError) as ei:

@@ -82,7 +82,7 @@ def test_manager_tables_drive_store_copy_and_decode(cuda):
     lens = np.array([len(seqs[s]) for s in order], np.int32)
     q = to_storage(rng.standard_normal((len(order), HKV * G, D), dtype=np.float32), "bf16")
     scale = 1.0 / np.sqrt(D)
-    for psize in (-2, -1, 0, 16):
+    for psize in (-3, -2, -1, 0, 16):
         out = pa.paged_attention_decode(np_to_torch(q, "bf16").to(cuda), k_cache, v_cache,
                                         torch.from_numpy(tables).to(cuda), torch.from_numpy(lens).to(cuda), scale,
                                         out_dtype=torch.float32, partition_size=psize)

@@ -86,7 +86,7 @@ def test_full_config_store_bit_exact_and_decode_parity(cuda, name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("psize", [-2, -1, 0, 16, 48, 512])
+@pytest.mark.parametrize("psize", [-3, -2, -1, 0, 16, 48, 512])
 @pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"])
 def test_launch_modes_agree_with_oracle(cuda, name, psize):
     _say(f"[gpu] modes {name} partition_size={psize}")
@@ -112,7 +112,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("psize", [-2, -1, 0, 16, 64])
+@pytest.mark.parametrize("psize", [-3, -2, -1, 0, 16, 64])
 def test_small_shapes_and_edges(cuda, case, psize):
     dt, b, hq, hkv, d, bs, lens = CASES[case]
     _say(f"[gpu] small case {CASES[case]} partition_size={psize}")
@@ -133,7 +133,7 @@ def test_length_one_returns_value_row_exactly(cuda):
     import paged_attention_decode_amd as pa
     x = make_inputs(custom_config(dtype="bf16", batch=4, hq=8, hkv=2, lens=(1, 1, 1, 1), seed=3))
     dev = to_device(x, cuda)
-    for psize in (-2, -1, 0):
+    for psize in (-3, -2, -1, 0):
         out = _run_step(dev, x, partition_size=psize).cpu().numpy()
         k2, v2, _ = oracle_after_store(x)
         geo = geometry(x)
@@ -344,7 +344,7 @@ def _fused_vs_two_calls(cuda, x, psize, out_dtype=None):
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("psize", [-2, -1, 0, 16])
+@pytest.mark.parametrize("psize", [-3, -2, -1, 0, 16])
 def test_fused_step_equals_store_then_decode(cuda, case, psize):
     dt, b, hq, hkv, d, bs, lens = CASES[case]
     _say(f"[gpu] fused step {CASES[case]} partition_size={psize}")
@@ -356,7 +356,7 @@ def test_fused_step_equals_store_then_decode(cuda, case, psize):
 
 
 @pytest.mark.parametrize("name,psize", [("qwen3_0p6b_bf16", 0), ("llama32_1b_fp16", 0), ("skewed_prefix_bf16", 0),
-                                        ("llama32_1b_fp16", 48)])
+                                        ("llama32_1b_fp16", 48), ("qwen3_0p6b_bf16", -3)])
 def test_fused_step_full_configs(cuda, name, psize):
     # psize 48 on the Llama shape needs more ranges than resident wavefronts (they loop)
     _say(f"[gpu] fused step full config {name} partition_size={psize}")
@@ -398,7 +398,7 @@ def test_fp16_many_tiny_weights_keep_their_precision(cuda):
     dev = dict(q=torch.from_numpy(q).to(cuda),
                k=torch.from_numpy(kc).view(geo.k_shape).to(cuda), v=torch.from_numpy(vc).view(geo.v_shape).to(cuda),
                bt=torch.from_numpy(bt).to(cuda), cl=torch.from_numpy(cl).to(cuda))
-    for psize in (-2, -1, 0, 512):
+    for psize in (-3, -2, -1, 0, 512):
         out = pa.paged_attention_decode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"], 0.125,
                                         out_dtype=torch.float32, partition_size=psize)
         torch.cuda.synchronize()

@@ -36,7 +36,7 @@ def test_largest_batch_in_every_mode(cuda):
     dev = to_device(x, cuda)
     seqs = list(range(0, len(lens), 181)) + [len(lens) - 1]
     _, _, ref = oracle_after_store(x, seqs=seqs)
-    for psize in (0, -2, -1, 512):
+    for psize in (0, -3, -2, -1, 512):
         _say(f"[gpu] 16383 sequences, partition_size={psize}")
         k_cache, v_cache = dev["k_cache"].clone(), dev["v_cache"].clone()
         pa.store_kvcache(dev["k_new"], dev["v_new"], dev["slot_mapping"], k_cache, v_cache)
@@ -80,7 +80,7 @@ def test_caches_past_4_gib(cuda):
 
     # store + decode in every mode, against the oracle's small case
     _, _, ref = oracle_after_store(x)
-    for psize in (0, -2, -1, 16):
+    for psize in (0, -3, -2, -1, 16):
         k_c, v_c = k_big.clone(), v_big.clone()
         pa.store_kvcache(dev["k_new"], dev["v_new"], slots, k_c, v_c)
         out = pa.paged_attention_decode(dev["q"], k_c, v_c, bt, dev["context_lens"], x.scale,
