@@ -74,6 +74,10 @@ def parse():
                     help="write profiles/decode_<workload>_kernel_trace.txt from a rocprofv3 --kernel-trace "
                          "--stats run of this script, then exit")
     ap.add_argument("--trace-command", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/<kernel>_<workload>_sq_counters.txt from rocprofv3 --pmc runs of SQ_ "
+                         "counters (the attention kernel, or the prefill kernel with --prefill), then exit")
+    ap.add_argument("--sq-commands", nargs="*", default=[], help="the profiling commands, recorded in the summary")
     return ap.parse_args()
 
 
@@ -198,6 +202,57 @@ def summarize_pmc(workload: str, fetch_dir: str, write_dir: str, commands) -> Pa
         f"hbm_write_bytes_per_launch: {write_b:.0f}",
         f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
     ]) + "\n")
+    return path
+
+
+def summarize_sq(workload: str, directories, commands, kernel: str = "decode") -> Path:
+    """SQ counters of one kernel, summed over its dispatches in each --pmc run, with derived shares.
+
+    Shares of SQ_WAVE_CYCLES are per wavefront: how much of its life a wavefront spent issuing
+    VALU, waiting for an instruction to issue, or waiting on s_waitcnt / a barrier. The MFMA pipe
+    busy fraction compares SQ_VALU_MFMA_BUSY_CYCLES with the kernel's SIMD-cycles, taken from the
+    run's timestamps at the box's 2.4 GHz peak clock, so it is a lower bound."""
+    import csv
+    name = "prefill" if kernel == "prefill" else "decode_kernel"
+    tot, disp, span = {}, {}, {}
+    for d in directories:
+        files = sorted(Path(d).rglob("*counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if name not in r["Kernel_Name"]:
+                    continue
+                c = r["Counter_Name"]
+                tot[c] = tot.get(c, 0.0) + float(r["Counter_Value"])
+                disp.setdefault(c, set()).add(r["Dispatch_Id"])
+                span[(d, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not tot:
+        raise SystemExit(f"no {name} rows")
+    lines = [f"# SQ counters of the {name} kernel on workload {workload}, summed over its dispatches",
+             *[f"# command: {c}" for c in commands],
+             f"# summary command: python bench.py --workload {workload} {'--prefill ' if kernel == 'prefill' else ''}"
+             f"--summarize-sq {' '.join(directories)}",
+             f"kernel_source_sha256: {kernel_source_sha('prefill' if kernel == 'prefill' else 'decode')}"]
+    for c in sorted(tot):
+        lines.append(f"{c}: {tot[c]:.6g} ({len(disp[c])} dispatches)")
+    def per(c):
+        return tot[c] / len(disp[c]) if c in tot else None
+    wc = per("SQ_WAVE_CYCLES")
+    if wc:
+        for c, label in (("SQ_ACTIVE_INST_VALU", "issuing VALU (incl. MFMA)"), ("SQ_WAIT_INST_ANY", "waiting to issue"),
+                         ("SQ_WAIT_ANY", "waiting on s_waitcnt or a barrier"), ("SQ_ACTIVE_INST_LDS", "issuing LDS")):
+            if per(c) is not None:
+                lines.append(f"share_of_wave_cycles {label}: {per(c) / wc:.3f}")
+    if per("SQ_INSTS_VALU") and per("SQ_INSTS_MFMA"):
+        lines.append(f"valu_instructions_per_mfma: {(per('SQ_INSTS_VALU') - per('SQ_INSTS_MFMA')) / per('SQ_INSTS_MFMA'):.2f}")
+    if per("SQ_VALU_MFMA_BUSY_CYCLES") and span:
+        mean_ns = sum(span.values()) / len(span)
+        simd_cycles = mean_ns * 1e-9 * 2.4e9 * 1024
+        lines.append(f"mfma_busy_fraction_at_2.4GHz: {per('SQ_VALU_MFMA_BUSY_CYCLES') / simd_cycles:.3f}")
+    path = PROFILES / f"{'prefill' if kernel == 'prefill' else 'decode'}_{workload}_sq_counters.txt"
+    PROFILES.mkdir(exist_ok=True)
+    path.write_text("\n".join(lines) + "\n")
     return path
 
 
@@ -400,6 +455,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         print(summarize_pmc(args.workload, args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands))
+        return
+    if args.summarize_sq:
+        print(summarize_sq(args.workload, args.summarize_sq, args.sq_commands, "prefill" if args.prefill else "decode"))
         return
     if args.summarize_trace:
         print(summarize_trace(args.workload, args.summarize_trace, args.trace_command,
