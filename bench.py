@@ -17,7 +17,7 @@ Prints ONE JSON line:
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample
                of the same workload (a reported baseline, not the target)
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload NAME] [--prefill]
 """
 
 from __future__ import annotations
@@ -395,6 +395,16 @@ def extra_timings(calls: dict, reps: int, stream_bytes: int, dev) -> dict:
     return out
 
 
+def prefill_useful_flops(head_dim: int, num_heads: int, new_tokens, context_lens) -> float:
+    """Useful flops of a causal paged prefill: 4*D*Hq per visible (query, key) pair. A sequence
+    with n new tokens among L sees n*L - n(n-1)/2 pairs (query i, at position L-n+i, sees
+    L-n+i+1 keys)."""
+    import numpy as np
+    n = np.asarray(new_tokens, dtype=np.float64)
+    L = np.asarray(context_lens, dtype=np.float64)
+    return 4.0 * head_dim * num_heads * float(np.sum(n * L - n * (n - 1) / 2))
+
+
 def prefill_bench(args) -> None:
     """Full-prompt causal prefill over the workload's paged caches; useful flops = 4*D*Hq*sum(n*L - n(n-1)/2)."""
     import numpy as np
@@ -424,7 +434,7 @@ def prefill_bench(args) -> None:
     cl = torch.from_numpy(x.context_lens).to(dev)
     qst = torch.from_numpy(qs).to(dev)
     out = torch.empty((int(qs[-1]), cfg.num_heads, cfg.head_dim), dtype=torch.float32, device=dev)
-    flops = 4.0 * cfg.head_dim * cfg.num_heads * float(np.sum(lens * lens - lens * (lens - 1) / 2))
+    flops = prefill_useful_flops(cfg.head_dim, cfg.num_heads, lens, lens)
     for _ in range(max(1, args.warmup)):
         pa.paged_prefill(q, k_cache, v_cache, bt, cl, qst, x.scale, out)
     torch.cuda.synchronize()
