@@ -475,8 +475,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the decode "
-              "path has no cross-GPU step in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the library "
+              "has no cross-GPU step; each GPU would run its own shard of sequences or kv heads", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
