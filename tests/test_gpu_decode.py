@@ -108,6 +108,7 @@ CASES = [
     ("fp32", 2, 8, 1, 64, 128, (129, 300)),
     ("bf16", 6, 8, 8, 128, 16, (0, 5, 0, 64, 3, 1)),   # empty contexts give zeros
     ("fp32", 2, 4, 2, 256, 16, (40, 77)),              # fp32 at head_dim 256 (largest register set)
+    ("bf16", 3, 32, 2, 256, 16, (70, 33, 16)),         # 16 heads at head_dim 256: workgroup split runs as one pass
 ]
 
 
