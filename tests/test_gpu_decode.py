@@ -118,8 +118,6 @@ def test_small_shapes_and_edges(cuda, case, psize):
     dt, b, hq, hkv, d, bs, lens = CASES[case]
     _say(f"[gpu] small case {CASES[case]} partition_size={psize}")
     x = make_inputs(custom_config(dtype=dt, batch=b, hq=hq, hkv=hkv, d=d, bs=bs, lens=lens, seed=100 + case))
-    # context length 0 has no token to store: skip its slot
-    x.slot_mapping[x.context_lens == 0] = -1
     dev = to_device(x, cuda)
     out = _run_step(dev, x, partition_size=psize).cpu().numpy()
     k2, v2, ref = oracle_after_store(x)
@@ -350,7 +348,6 @@ def test_fused_step_equals_store_then_decode(cuda, case, psize):
     dt, b, hq, hkv, d, bs, lens = CASES[case]
     _say(f"[gpu] fused step {CASES[case]} partition_size={psize}")
     x = make_inputs(custom_config(dtype=dt, batch=b, hq=hq, hkv=hkv, d=d, bs=bs, lens=lens, seed=200 + case))
-    x.slot_mapping[x.context_lens == 0] = -1   # no token to store for an empty context
     out = _fused_vs_two_calls(cuda, x, psize).cpu().numpy()
     _, _, ref = oracle_after_store(x)
     assert np.abs(out - ref).max() <= TOL[dt]

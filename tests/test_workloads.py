@@ -39,6 +39,18 @@ def test_store_slots_unique_and_at_last_position(name):
         assert x.slot_mapping[s] // bs not in set(x.shared_blocks)
 
 
+def test_empty_contexts_store_nothing():
+    # An empty context has no position L-1: its slot is -1 (skipped), so two empty sequences never
+    # share a slot and the fused step (which writes position L-1) and store_kvcache agree.
+    from workloads import Config
+    cfg = Config(name="custom", dtype="bf16", batch=6, num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                 lengths="list", len_list=(0, 5, 0, 64, 3, 1), seed=1)
+    x = make_inputs(cfg, structure_only=True)
+    assert x.slot_mapping.tolist()[0] == -1 and x.slot_mapping.tolist()[2] == -1
+    live = [int(v) for v, L in zip(x.slot_mapping, x.context_lens) if L > 0]
+    assert all(v >= 0 for v in live) and len(set(live)) == len(live)
+
+
 def test_length_distributions():
     c = make_inputs(get_config("tiny_fp32"), structure_only=True)
     assert c.context_lens.tolist() == [1, 17, 33, 64] and c.num_blocks == 32

@@ -88,7 +88,7 @@ class Inputs:
     q: np.ndarray                 # [B, Hq, D] storage
     k_new: np.ndarray             # [B, Hkv, D] storage
     v_new: np.ndarray
-    slot_mapping: np.ndarray      # [B] int32: slot of token L-1 of each sequence
+    slot_mapping: np.ndarray      # [B] int32: slot of token L-1 of each sequence (-1 when L = 0)
     scale: float
     unused_blocks: List[int] = field(default_factory=list)
     shared_blocks: List[int] = field(default_factory=list)
@@ -167,6 +167,8 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, structure_only: bool = 
     bs = cfg.block_size
     pos = lens.astype(np.int64) - 1
     slots = (tables[np.arange(cfg.batch), pos // bs].astype(np.int64) * bs + pos % bs).astype(np.int32)
+    # An empty context has no token at position L-1: nothing to store (a negative slot is skipped).
+    slots[lens == 0] = -1
     if structure_only:
         empty = np.zeros(0, np.float32)
         return Inputs(cfg=cfg, context_lens=lens, block_tables=tables, num_blocks=pool,
