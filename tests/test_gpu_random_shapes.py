@@ -1,4 +1,5 @@
-"""GPU parity on seeded random shapes: decode (every partition mode), the fused step and prefill.
+"""GPU parity on seeded random shapes: decode (every partition mode), the fused step, prefill, and
+multi-token stores.
 
 Each case draws a dtype, head_dim, block size, kv heads, group size (including sizes that do not
 divide 16 and groups above 16), a batch, and context lengths mixing 0, 1, tile and block edges
@@ -107,3 +108,52 @@ def test_random_shape(cuda, case):
     torch.cuda.synchronize()
     ref_p = oracle.prefill(q, k2, v2, x.block_tables, x.context_lens, qs, x.scale, geometry(x))
     assert np.abs(pre.cpu().numpy() - ref_p).max() <= TOL[dt]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_multi_token_store(cuda, case):
+    """store_kvcache of many tokens (a prompt's worth): runs of consecutive slots, scattered
+    slots, skipped (negative) slots and token rows wider than Hkv*D, bit for bit over the whole
+    caches against the oracle's scatter."""
+    import torch
+    import paged_attention_decode_amd as pa
+    rng = np.random.default_rng(80000 + case)
+    dt = str(rng.choice(["fp32", "fp16", "bf16"]))
+    d = int(rng.choice([64, 128, 256]))
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    hkv = int(rng.integers(1, 5))
+    nb = int(rng.integers(4, 24))
+    num_slots = nb * bs
+    # a run of consecutive slots (a prompt written in order), then scattered unique slots
+    run = int(rng.integers(1, min(num_slots, 300) + 1))
+    start = int(rng.integers(0, num_slots - run + 1))
+    chosen = list(range(start, start + run))
+    rest = [int(s) for s in rng.permutation(num_slots) if not start <= s < start + run]
+    chosen += rest[:int(rng.integers(0, min(len(rest), 200) + 1))]
+    slots = np.array(chosen, dtype=np.int32)
+    slots[rng.random(len(slots)) < 0.1] = -1
+    rng.shuffle(slots)
+    n = len(slots)
+    _say(f"[gpu] random store {case}: {dt} D={d} bs={bs} Hkv={hkv} blocks={nb} tokens={n}")
+    geo = oracle.CacheGeometry(nb, hkv, d, bs, dt)
+    elems = nb * hkv * bs * d
+    k_cache = to_storage(rng.standard_normal(elems, dtype=np.float32), dt)
+    v_cache = to_storage(rng.standard_normal(elems, dtype=np.float32), dt)
+    pad = int(rng.choice([0, 8, 64]))
+    k_rows = to_storage(rng.standard_normal((n, hkv * d + pad), dtype=np.float32), dt)
+    v_rows = to_storage(rng.standard_normal((n, hkv * d + pad), dtype=np.float32), dt)
+    k_new = np.ascontiguousarray(k_rows[:, :hkv * d]).reshape(n, hkv, d)
+    v_new = np.ascontiguousarray(v_rows[:, :hkv * d]).reshape(n, hkv, d)
+    k2, v2 = oracle.store_kvcache(k_new, v_new, slots, k_cache, v_cache, geo)
+
+    tdt = torch_dtype(dt)
+    kc = np_to_torch(k_cache, dt).view(pa.k_cache_shape(nb, hkv, d, bs, tdt)).to(cuda)
+    vc = np_to_torch(v_cache, dt).view(pa.v_cache_shape(nb, hkv, d, bs)).to(cuda)
+    kr = np_to_torch(k_rows, dt).to(cuda)
+    vr = np_to_torch(v_rows, dt).to(cuda)
+    kn = kr[:, :hkv * d].view(n, hkv, d)   # token stride hkv*d + pad
+    vn = vr[:, :hkv * d].view(n, hkv, d)
+    pa.store_kvcache(kn, vn, torch.from_numpy(slots).to(cuda), kc, vc)
+    torch.cuda.synchronize()
+    assert torch_to_np(kc, dt).reshape(-1).tobytes() == k2.reshape(-1).tobytes()
+    assert torch_to_np(vc, dt).reshape(-1).tobytes() == v2.reshape(-1).tobytes()
