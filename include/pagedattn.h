@@ -369,7 +369,12 @@ const char* pa_last_error(void);
 /* Library version string, e.g. "libpagedattn 0.1.0 gfx950". */
 const char* pa_version(void);
 
-/* Frees the library-owned workspaces of all devices. Returns PA_OK or PA_ERR_HIP. */
+/*
+ * Frees the library-owned workspaces of all devices. hipFree waits for the
+ * device's queued work first, so kernels already launched finish with their
+ * workspace; no decode call may run concurrently with this one. A later decode
+ * call allocates a workspace again. Returns PA_OK or PA_ERR_HIP.
+ */
 int pa_shutdown(void);
 
 #ifdef __cplusplus
