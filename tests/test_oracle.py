@@ -374,6 +374,10 @@ def _sdpa_causal(q64, k64, v64, scale, offset):
 def test_prefill_matches_sdpa_with_causal_offset_mask(seed, g, hkv, dtype, data):
     lens = data.draw(st.lists(st.integers(1, 40), min_size=1, max_size=3))
     news = [data.draw(st.integers(1, L)) for L in lens]
+    _prefill_vs_sdpa(seed, g, hkv, dtype, lens, news)
+
+
+def _prefill_vs_sdpa(seed, g, hkv, dtype, lens, news):
     rng = np.random.default_rng(seed)
     d = 16
     case = PagedCase(rng, len(lens), g * hkv, hkv, d, 8, lens, dtype=dtype)
@@ -406,3 +410,65 @@ def test_prefill_first_token_returns_its_value_row():
                          case.geometry())
     for h in range(4):
         np.testing.assert_array_equal(out[0, h], widen_np(case.v_dense[0][0, h // 2], "fp32"))
+
+
+# ---------------------------------------------------------------- planted mistakes: prefill and merge
+
+def _prefill_seeing(position):
+    """The oracle's prefill with another rule for the last key query i may see (a planted mistake)."""
+    def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, geo, seqs=None):
+        t_total, hq, dim = q.shape
+        qf = oracle.widen(q, geo.dtype)
+        group = hq // geo.num_kv_heads
+        sigma = float(np.float32(scale))
+        out = np.zeros((t_total, hq, dim))
+        for s in range(len(context_lens)):
+            q0, q1 = int(query_start[s]), int(query_start[s + 1])
+            n, length = q1 - q0, int(context_lens[s])
+            if n == 0:
+                continue
+            k, v = oracle.gather_kv(k_cache, v_cache, block_tables[s], length, geo)
+            for i in range(n):
+                p = position(length, n, i)
+                for h in range(hq):
+                    z = sigma * (k[:p + 1, h // group, :] @ qf[q0 + i, h])
+                    e = np.exp(z - z.max())
+                    out[q0 + i, h] = (e / e.sum()) @ v[:p + 1, h // group, :]
+        return out
+    return prefill
+
+
+def _merge_flipped(lse, parts):
+    finite = np.isfinite(lse)
+    m = lse[finite].max()
+    w = np.where(finite, np.exp(m - np.where(finite, lse, m)), 0.0)  # sign of the exponent flipped
+    return (w[:, None] * np.where(finite[:, None], parts, 0.0)).sum(axis=0) / w.sum()
+
+
+def _merge_unnormalised(lse, parts):
+    finite = np.isfinite(lse)
+    m = lse[finite].max()
+    w = np.where(finite, np.exp(np.where(finite, lse, m) - m), 0.0)
+    return (w[:, None] * np.where(finite[:, None], parts, 0.0)).sum(axis=0)  # no division by the weight sum
+
+
+@pytest.mark.parametrize("mutant", ["future_token", "no_prefix_offset", "merge_sign", "merge_unnormalised"])
+def test_prefill_and_merge_pins_catch_planted_mistakes(monkeypatch, mutant):
+    if mutant in ("future_token", "no_prefix_offset"):
+        rule = (lambda L, n, i: min(L - n + i + 1, L - 1)) if mutant == "future_token" else (lambda L, n, i: i)
+        # the pins call the package's name for it
+        monkeypatch.setattr(oracle, "prefill", _prefill_seeing(rule))
+    elif mutant == "merge_sign":
+        monkeypatch.setattr(opa, "merge_partitions", _merge_flipped)
+    else:
+        monkeypatch.setattr(opa, "merge_partitions", _merge_unnormalised)
+    pins = [test_prefill_of_one_new_token_is_decode, test_prefill_first_token_returns_its_value_row,
+            lambda: _prefill_vs_sdpa(5, 2, 2, "fp32", [9, 17], [4, 17]),
+            lambda: test_split_merge_equals_dense(7), lambda: test_split_merge_equals_dense(16)]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin caught the planted {mutant} mistake"
