@@ -472,3 +472,32 @@ def test_prefill_and_merge_pins_catch_planted_mistakes(monkeypatch, mutant):
         except AssertionError:
             failed += 1
     assert failed >= 1, f"no pin caught the planted {mutant} mistake"
+
+
+def _v_index_swapped(geo, b, g, o, d):
+    return (b, g, o % (geo.block_size // 4), d, o // (geo.block_size // 4))  # token group and position exchanged
+
+
+def _store_next_slot(k_new, v_new, slot_mapping, k_cache, v_cache, geo):
+    shifted = np.where(np.asarray(slot_mapping) >= 0, np.asarray(slot_mapping) + 1, -1)
+    shifted = np.where(shifted >= geo.num_blocks * geo.block_size, 0, shifted)
+    return opa.__dict__["_orig_store"](k_new, v_new, shifted, k_cache, v_cache, geo)
+
+
+@pytest.mark.parametrize("mutant", ["v_layout", "store_next_slot"])
+def test_layout_and_store_pins_catch_planted_mistakes(monkeypatch, mutant):
+    if mutant == "v_layout":
+        monkeypatch.setattr(opa, "v_index", _v_index_swapped)
+    else:
+        monkeypatch.setitem(opa.__dict__, "_orig_store", opa.store_kvcache)
+        monkeypatch.setattr(oracle, "store_kvcache", _store_next_slot)
+    pins = [lambda: test_gather_matches_transpose_construction("fp16", 8), test_layout_golden_positions,
+            lambda: test_store_matches_logical_assignment_and_leaves_other_bytes("bf16"),
+            test_store_then_decode_sees_new_token]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"no pin caught the planted {mutant} mistake"
