@@ -274,6 +274,19 @@ def summarize_trace(workload: str, directory: str, command: str, kernel: str = "
         lines.append(f"{name:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
                      f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
                      f"{float(r['Percentage']):>6.2f}")
+    # The timed launches alone (the trace's average also counts the warm-up launches): the last
+    # --steps launches of the main kernel, in start order.
+    import re
+    traces = sorted(Path(directory).rglob("*kernel_trace.csv"))
+    m = re.search(r"--steps\s+(\d+)", command)
+    main_name = "prefill" if kernel == "prefill" else "decode_kernel"
+    if traces and m:
+        launches = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                          for r in csv.DictReader(open(traces[0])) if main_name in r["Kernel_Name"])
+        timed = [d for _, d in launches][-int(m.group(1)):]
+        if timed:
+            lines.append(f"timed_launches: {len(timed)} (the last --steps launches of the {main_name} kernel)")
+            lines.append(f"timed_launches_mean_us: {sum(timed) / len(timed) / 1e3:.2f}")
     path = PROFILES / f"{kernel}_{workload}_kernel_trace.txt"
     PROFILES.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")

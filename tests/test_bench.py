@@ -75,10 +75,16 @@ def test_trace_summary_lists_every_kernel(profiles, tmp_path):
             ["void pa::(anonymous namespace)::reduce_kernel<2, 128>(pa::DecodeArgs)", 13, 7.0e4, 5410.0, 2.1, 4960.0,
              6800.0, 1.0]]
     _write_csv(tmp_path / "t" / "run_kernel_stats.csv", hdr, rows)
-    path = bench.summarize_trace("wl", str(tmp_path / "t"), "the command")
+    # per-launch trace: 3 warm-up launches (slow) then 2 timed ones, with a merge kernel between
+    k = "void pa::(anonymous namespace)::decode_kernel<2, 128, false>(pa::DecodeArgs)"
+    trace = [[k, 0, 300000], ["reduce_kernel", 300000, 305000], [k, 400000, 690000], [k, 800000, 1050000],
+             [k, 1100000, 1320000], [k, 1400000, 1630000]]
+    _write_csv(tmp_path / "t" / "run_kernel_trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], trace)
+    path = bench.summarize_trace("wl", str(tmp_path / "t"), "rocprofv3 ... -- python -u bench.py --steps 2")
     text = path.read_text()
     assert path.name == "decode_wl_kernel_trace.txt"
-    assert "# command: the command" in text and "anonymous namespace" not in text
+    assert "# command: rocprofv3 ... --steps 2" in text and "anonymous namespace" not in text
+    assert "timed_launches: 2" in text and "timed_launches_mean_us: 225.00" in text
     assert "228.99" in text and "5.41" in text
     assert f"kernel_source_sha256: {bench.kernel_source_sha()}" in text
 
