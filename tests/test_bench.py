@@ -83,7 +83,7 @@ def test_trace_summary_lists_every_kernel(profiles, tmp_path):
     path = bench.summarize_trace("wl", str(tmp_path / "t"), "rocprofv3 ... -- python -u bench.py --steps 2")
     text = path.read_text()
     assert path.name == "decode_wl_kernel_trace.txt"
-    assert "# command: rocprofv3 ... --steps 2" in text and "anonymous namespace" not in text
+    assert "# command: rocprofv3 ... -- python -u bench.py --steps 2" in text and "anonymous namespace" not in text
     assert "timed_launches: 2" in text and "timed_launches_mean_us: 225.00" in text
     assert "228.99" in text and "5.41" in text
     assert f"kernel_source_sha256: {bench.kernel_source_sha()}" in text
