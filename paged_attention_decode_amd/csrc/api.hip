@@ -10,7 +10,6 @@
 #include <climits>
 #include <mutex>
 #include <string>
-#include <vector>
 
 namespace {
 
@@ -55,8 +54,11 @@ struct DeviceState {
   size_t ws_bytes = 0;
 };
 
+// Fixed storage, so a DeviceState pointer stays valid while other threads
+// initialise further devices.
+constexpr int kMaxDevices = 64;
 std::mutex g_mutex;
-std::vector<DeviceState> g_devices;
+DeviceState g_devices[kMaxDevices];
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -174,8 +176,8 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
 int device_state(DeviceState** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
   std::lock_guard<std::mutex> lock(g_mutex);
-  if ((int)g_devices.size() <= dev) g_devices.resize(dev + 1);
   DeviceState& st = g_devices[dev];
   if (!st.init) {
     int cus = 0;
@@ -535,10 +537,10 @@ int pa_shutdown(void) {
   int rc = PA_OK;
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) cur = -1;
-  for (size_t d = 0; d < g_devices.size(); ++d) {
+  for (int d = 0; d < kMaxDevices; ++d) {
     DeviceState& st = g_devices[d];
     if (!st.ws) continue;
-    if (hipSetDevice((int)d) != hipSuccess || hipFree(st.ws) != hipSuccess) rc = PA_ERR_HIP;
+    if (hipSetDevice(d) != hipSuccess || hipFree(st.ws) != hipSuccess) rc = PA_ERR_HIP;
     st.ws = nullptr;
     st.ws_bytes = 0;
   }
