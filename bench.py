@@ -51,6 +51,9 @@ def parse():
                     help="0 automatic, -1 one pass, -2 balanced split, >0 fixed ranges of that many tokens")
     ap.add_argument("--cached-prefix-tokens", type=int, default=0,
                     help="leading tokens per context read with cached loads (0 library default, -1 none)")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="read the leading blocks that neighbouring sequences share once per group "
+                         "(pa_decode_opts.shared_prefix; the sharing is found on the device)")
     ap.add_argument("--fused-step", action="store_true",
                     help="run each step as one pa_decode_step launch (scatter fused into the attention kernel)")
     ap.add_argument("--prefill", action="store_true",
@@ -529,12 +532,13 @@ def main():
         if args.fused_step:
             pa.decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, x.scale, out,
                            partition_size=args.partition_size, cached_prefix_tokens=args.cached_prefix_tokens,
-                           events=events)
+                           events=events, shared_prefix=args.shared_prefix)
             return
         pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache)
         pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
                                   partition_size=args.partition_size,
-                                  cached_prefix_tokens=args.cached_prefix_tokens, events=events)
+                                  cached_prefix_tokens=args.cached_prefix_tokens, events=events,
+                                  shared_prefix=args.shared_prefix)
 
     # A plain copy of known size (COPY_BYTES read + written): counter runs scale HBM bytes by it.
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -589,6 +593,10 @@ def main():
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     mean_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     achieved = kv_bytes / (mean_kernel_ms * 1e-3) / 1e9
+    # The distinct K/V bytes of the batch (a block shared by several sequences counted once): the
+    # least any kernel must read. Logical bytes above it are re-reads that caches or the
+    # shared-prefix option serve.
+    achieved_unique = x.unique_kv_bytes / (mean_kernel_ms * 1e-3) / 1e9
 
     # Steps timed after overwriting 1 GiB, so last-level caches hold no KV (reported beside the main figure).
     cold = []
@@ -625,14 +633,16 @@ def main():
 
     # Per-call distributions, outside the timed region above. The store here rewrites the same
     # slots with the same rows, so the cache contents do not change.
-    def decode_with(psize):
+    def decode_with(psize, shared=args.shared_prefix):
         return lambda: pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
                                                  partition_size=psize,
-                                                 cached_prefix_tokens=args.cached_prefix_tokens)
+                                                 cached_prefix_tokens=args.cached_prefix_tokens,
+                                                 shared_prefix=shared)
     calls = {"store": lambda: pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache),
              "decode": decode_with(args.partition_size), "store_plus_decode": step}
     for psize, name in ((-2, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
-        calls[name] = decode_with(psize)
+        calls[name] = decode_with(psize, False)
+    calls["decode_balanced_shared_prefix"] = decode_with(-2, True)
     timings = None
     if not args.no_extra_timings:
         timings = extra_timings(calls, 20, 2 << 30, dev)
@@ -646,7 +656,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the workload)",
         "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
-                       partition_size=args.partition_size,
+                       partition_size=args.partition_size, shared_prefix=bool(args.shared_prefix),
                        cached_prefix_tokens=args.cached_prefix_tokens or pa.DEFAULT_CACHED_PREFIX_TOKENS,
                        launch="hip graph replay" if args.graph else "eager",
                        step="pa_decode_step (fused scatter + attention)" if args.fused_step
@@ -655,7 +665,9 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_kernel (attention, excludes store and merge)",
+                     "achieved_on_unique_bytes": round(achieved_unique, 2),
+                     "kernel": "decode_kernel (attention, excludes store and merge; with the shared-prefix "
+                               "option also its detection kernel)",
                      "kernel_mean_ms": round(mean_kernel_ms, 5),
                      "cold_kernel_median_ms": round(sorted(cold)[len(cold) // 2], 5) if cold else None},
     }

@@ -191,11 +191,31 @@ int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_
  *       never stream. Changes speed only, never results.
  * workspace / workspace_bytes: device memory used instead of the library's own
  *       (NULL = library-owned). Must be 256-byte aligned and at least
- *       pa_decode_workspace_bytes(...) bytes. Its contents need no
- *       initialisation. Calls that share a workspace must not overlap.
+ *       pa_decode_workspace_bytes(...) bytes (pa_decode_plan_ex's figure with
+ *       shared_prefix). Its contents need no initialisation. Calls that share
+ *       a workspace must not overlap.
  * event_begin / event_end: optional hipEvent_t handles (as void*) recorded on
  *       `stream` immediately before and after the attention kernel itself (not
- *       the reduce kernel), so callers can time that kernel alone.
+ *       the reduce kernel), so callers can time that kernel alone. With
+ *       shared_prefix they also enclose the detection kernel.
+ * shared_prefix: nonzero = read shared prefixes once. Prefix caching (miniVLLM
+ *       docs, "What is miniVLLM?") lets sequences share the physical blocks of
+ *       a common prefix. With this option a first small kernel finds, in each
+ *       window of W = 16 / G consecutive sequences, the group whose leading
+ *       block-table entries are identical (equal physical ids, so equal K/V),
+ *       and the prefix length that saves the most reads. It counts only whole
+ *       blocks before each sequence's last-token block, and groups need a
+ *       prefix of two 16-token tiles or more. The attention kernel then streams
+ *       the group's prefix once, the G query heads of the group's sequences
+ *       filling the 16 columns of one matrix-core tile. Each sequence streams
+ *       its own remaining tiles, and the reduce kernel merges its partials with
+ *       the prefix's (the same log-sum-exp merge). The result is the same
+ *       attention (a different summation order). Sharing is verified on the device
+ *       from the block tables, so the option is a hint that costs time when
+ *       nothing is shared and never changes what is computed. Applies only in
+ *       the split modes (-2 or a fixed size; with the automatic mode, where it
+ *       picks them), with G <= 8 and num_seqs <= 8191; otherwise ignored. The
+ *       workspace grows: see pa_decode_plan_ex.
  */
 #define PA_DEFAULT_CACHED_PREFIX_TOKENS 1024
 
@@ -206,6 +226,7 @@ typedef struct pa_decode_opts {
   size_t workspace_bytes;
   void* event_begin;
   void* event_end;
+  int32_t shared_prefix;
 } pa_decode_opts;
 
 int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void* v_cache,
@@ -288,7 +309,19 @@ int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, in
                    int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce,
                    size_t* workspace_bytes);
 
-/* Workspace bytes pa_paged_attention_decode_ex needs for these sizes (0 on bad arguments). */
+/*
+ * pa_decode_plan_ex - the same plan for a call with these options (partition_size
+ * and shared_prefix are read; opts may be NULL). Also fills shared_prefix_window:
+ * the sequences per shared-prefix window, 0 when shared prefixes do not apply.
+ */
+int pa_decode_plan_ex(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t max_blocks_per_seq, int32_t dtype,
+                      const pa_decode_opts* opts, int32_t num_cus,
+                      int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce,
+                      int32_t* shared_prefix_window, size_t* workspace_bytes);
+
+/* Workspace bytes pa_paged_attention_decode_ex needs for these sizes without shared_prefix
+ * (0 on bad arguments). */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                  int32_t dtype, int32_t partition_size);

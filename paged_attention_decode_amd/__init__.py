@@ -57,6 +57,7 @@ class DecodeOpts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("event_begin", ctypes.c_void_p),
         ("event_end", ctypes.c_void_p),
+        ("shared_prefix", ctypes.c_int32),
     ]
 
 
@@ -90,6 +91,10 @@ def load_library():
     lib.pa_decode_plan.argtypes = [c_int] * 9 + [ctypes.POINTER(c_i64), ctypes.POINTER(c_int),
                                                  ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_plan.restype = c_int
+    lib.pa_decode_plan_ex.argtypes = [c_int] * 7 + [ctypes.POINTER(DecodeOpts), c_int, ctypes.POINTER(c_i64),
+                                                    ctypes.POINTER(c_int), ctypes.POINTER(c_int),
+                                                    ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_decode_plan_ex.restype = c_int
     lib.pa_decode_workspace_bytes.argtypes = [c_int] * 8
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_last_error.argtypes = []
@@ -231,7 +236,7 @@ def store_kvcache(k, v, slot_mapping, k_cache, v_cache) -> None:
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
                            out_dtype=None, partition_size: int = 0, cached_prefix_tokens: int = 0,
-                           workspace=None, events=None):
+                           workspace=None, events=None, shared_prefix: bool = False):
     """Decode attention; returns ``out`` ([B, Hq, D], fp32 or q's dtype).
 
     partition_size: 0 automatic (default: one pass when max_blocks_per_seq *
@@ -241,7 +246,9 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     of each context read with cached loads, the rest streamed (0 library
     default, -1 stream all; speed only). workspace: optional uint8 CUDA tensor
     (see ``workspace_bytes``). events: optional (begin, end) torch.cuda.Event
-    pair recorded around the attention kernel itself.
+    pair recorded around the attention kernel itself. shared_prefix: read the
+    leading blocks that neighbouring sequences share (same physical ids) once
+    per group; found on the device, split modes only (see pa_decode_opts).
     """
     import torch
     lib = _lib or load_library()
@@ -270,6 +277,7 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     opts = DecodeOpts()
     opts.partition_size = int(partition_size)
     opts.cached_prefix_tokens = int(cached_prefix_tokens)
+    opts.shared_prefix = 1 if shared_prefix else 0
     if workspace is not None:
         _require_cuda(q, workspace)
         opts.workspace = workspace.data_ptr()
@@ -289,7 +297,7 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
 
 def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale: float, out=None, *,
                 out_dtype=None, partition_size: int = 0, cached_prefix_tokens: int = 0, workspace=None,
-                events=None):
+                events=None, shared_prefix: bool = False):
     """Fused decode step: write k_new/v_new ([B, Hkv, D]) at position L-1 of each sequence and attend.
 
     Same result as store_kvcache (at each sequence's last position) followed by
@@ -325,6 +333,7 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
     opts = DecodeOpts()
     opts.partition_size = int(partition_size)
     opts.cached_prefix_tokens = int(cached_prefix_tokens)
+    opts.shared_prefix = 1 if shared_prefix else 0
     if workspace is not None:
         _require_cuda(q, workspace)
         opts.workspace = workspace.data_ptr()
@@ -377,22 +386,29 @@ def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, 
 
 
 def decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype_code,
-                partition_size=0, num_cus=256) -> dict:
+                partition_size=0, num_cus=256, shared_prefix=False) -> dict:
     """Host-only launch plan (no device access when num_cus > 0)."""
     lib = load_library()
     waves = ctypes.c_int64()
     rng = ctypes.c_int32()
     red = ctypes.c_int32()
+    win = ctypes.c_int32()
     ws = ctypes.c_size_t()
-    _check(lib.pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                              dtype_code, partition_size, num_cus, ctypes.byref(waves), ctypes.byref(rng),
-                              ctypes.byref(red), ctypes.byref(ws)))
+    opts = DecodeOpts()
+    opts.partition_size = int(partition_size)
+    opts.shared_prefix = 1 if shared_prefix else 0
+    _check(lib.pa_decode_plan_ex(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                 dtype_code, ctypes.byref(opts), num_cus, ctypes.byref(waves), ctypes.byref(rng),
+                                 ctypes.byref(red), ctypes.byref(win), ctypes.byref(ws)))
     return {"num_waves": waves.value, "range_tokens": rng.value, "uses_reduce": bool(red.value),
-            "workspace_bytes": ws.value}
+            "shared_prefix_window": win.value, "workspace_bytes": ws.value}
 
 
 def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype_code,
-                    partition_size=0) -> int:
+                    partition_size=0, shared_prefix=False) -> int:
+    if shared_prefix:
+        return decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype_code,
+                           partition_size, 0, shared_prefix=True)["workspace_bytes"]
     return int(load_library().pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                                        max_blocks_per_seq, dtype_code, partition_size))
 

@@ -78,7 +78,10 @@ struct Plan {
   bool reduce = false;
   size_t lds = 0;
   int n_hg = 0, gh_max = 0, segs_per_seq = 0;
-  size_t off_lse = 0, off_meta = 0, ws_bytes = 0;
+  int casc_width = 0;  // shared-prefix window (0: off)
+  int ws_cols = 0;     // partial-output columns per (range, slot)
+  int64_t whole_own_row = 0, whole_pre_row = 0;
+  size_t off_lse = 0, off_meta = 0, off_meta_pre = 0, off_share = 0, ws_bytes = 0;
 };
 
 bool valid_dtype(int dt) { return dt == PA_DTYPE_F32 || dt == PA_DTYPE_F16 || dt == PA_DTYPE_BF16; }
@@ -107,7 +110,7 @@ int check_decode_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
 }
 
 int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-              int32_t max_blocks, int32_t partition_size, int num_cus, Plan* p) {
+              int32_t max_blocks, int32_t partition_size, bool shared_prefix, int num_cus, Plan* p) {
   const int group = num_heads / num_kv_heads;
   p->n_hg = (group + kHeadsPerTile - 1) / kHeadsPerTile;
   p->gh_max = group < kHeadsPerTile ? group : kHeadsPerTile;
@@ -161,12 +164,31 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
   if (waves < 1) waves = 1;
   p->grid = (int)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
   p->num_waves = (int64_t)p->grid * kWavesPerGroup;
+  // Shared prefixes need the split modes' merge, two or more sequences' head groups per
+  // 16-column tile, and the sharing words in LDS beside the prefix sums.
+  p->casc_width = 0;
+  p->ws_cols = p->gh_max;
+  if (shared_prefix && p->reduce && p->n_hg == 1 && kHeadsPerTile / group >= 2 && num_seqs <= kMaxSharedSeqs) {
+    p->casc_width = kHeadsPerTile / group;
+    p->ws_cols = kHeadsPerTile;
+    p->lds += (size_t)num_seqs * sizeof(int32_t);
+  }
   if (p->reduce) {
     if (p->range_tiles == 0 || p->num_ranges < p->num_waves) p->num_ranges = p->num_waves;
-    const size_t rows = (size_t)p->num_ranges * 2 * p->gh_max;
+    const size_t windows = p->casc_width > 0 ? ((size_t)num_seqs + p->casc_width - 1) / p->casc_width : 0;
+    // Rows of pieces cut by range boundaries; with shared prefixes also rows for whole segments
+    // that are merged with a prefix (own segments of group members, and prefix segments).
+    p->whole_own_row = (int64_t)p->num_ranges * 2 * p->ws_cols;
+    p->whole_pre_row = p->whole_own_row + (p->casc_width > 0 ? segs * p->gh_max : 0);
+    const size_t rows = (size_t)p->whole_pre_row + windows * p->segs_per_seq * kHeadsPerTile;
     p->off_lse = align256(rows * head_dim * sizeof(float));
     p->off_meta = p->off_lse + align256(rows * sizeof(float));
     p->ws_bytes = p->off_meta + align256((size_t)segs * sizeof(int4));
+    if (p->casc_width > 0) {
+      p->off_meta_pre = p->ws_bytes;
+      p->off_share = p->off_meta_pre + align256(windows * p->segs_per_seq * sizeof(int4));
+      p->ws_bytes = p->off_share + align256((size_t)num_seqs * sizeof(int32_t));
+    }
   } else {
     p->off_lse = p->off_meta = p->ws_bytes = 0;
   }
@@ -333,9 +355,11 @@ int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache,
   return ok();
 }
 
-int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                   int32_t max_blocks_per_seq, int32_t dtype, int32_t partition_size, int32_t num_cus,
-                   int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce, size_t* workspace_bytes) {
+int pa_decode_plan_ex(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t max_blocks_per_seq, int32_t dtype, const pa_decode_opts* opts,
+                      int32_t num_cus, int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce,
+                      int32_t* shared_prefix_window, size_t* workspace_bytes) {
+  const int32_t partition_size = opts ? opts->partition_size : 0;
   int rc = check_decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
                               partition_size);
   if (rc != PA_OK) return rc;
@@ -347,13 +371,23 @@ int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, in
   }
   Plan p;
   rc = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, partition_size,
-                 num_cus, &p);
+                 opts && opts->shared_prefix != 0, num_cus, &p);
   if (rc != PA_OK) return rc;
   if (num_waves) *num_waves = p.num_waves;
   if (range_tokens) *range_tokens = p.range_tiles > 0 ? p.range_tiles * kTile : p.range_tiles;
   if (uses_reduce) *uses_reduce = p.reduce ? 1 : 0;
+  if (shared_prefix_window) *shared_prefix_window = p.casc_width;
   if (workspace_bytes) *workspace_bytes = p.ws_bytes;
   return ok();
+}
+
+int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t max_blocks_per_seq, int32_t dtype, int32_t partition_size, int32_t num_cus,
+                   int64_t* num_waves, int32_t* range_tokens, int32_t* uses_reduce, size_t* workspace_bytes) {
+  pa_decode_opts o = {};
+  o.partition_size = partition_size;
+  return pa_decode_plan_ex(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype, &o,
+                           num_cus, num_waves, range_tokens, uses_reduce, nullptr, workspace_bytes);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -398,7 +432,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
   rc = device_state(&st);
   if (rc != PA_OK) return rc;
   Plan p;
-  rc = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, psize, st->num_cus, &p);
+  rc = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, psize,
+                 opts && opts->shared_prefix != 0, st->num_cus, &p);
   if (rc != PA_OK) return rc;
 
   char* ws = nullptr;
@@ -438,6 +473,13 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
   a.ws_o = ws ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_lse = ws ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
   a.ws_meta = ws ? reinterpret_cast<int4*>(ws + p.off_meta) : nullptr;
+  a.ws_meta_pre = (ws && p.casc_width > 0) ? reinterpret_cast<int4*>(ws + p.off_meta_pre) : nullptr;
+  a.ws_share = (ws && p.casc_width > 0) ? reinterpret_cast<int32_t*>(ws + p.off_share) : nullptr;
+  a.ws_cols = p.ws_cols;
+  a.whole_own_row = p.whole_own_row;
+  a.whole_pre_row = p.whole_pre_row;
+  // A prefix piece addresses the query rows of a whole window from one buffer resource.
+  a.casc_width = ((int64_t)p.casc_width * q_seq_stride * e < INT32_MAX) ? p.casc_width : 0;
   a.q_seq_stride = q_seq_stride;
   a.num_blocks = num_blocks;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -468,7 +510,12 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
     hipError_t err = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->event_begin), s);
     if (err != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord(begin) failed: %s", hipGetErrorString(err));
   }
-  hipError_t err = launch_decode(a, dtype, head_dim, p.grid, p.lds, s);
+  hipError_t err;
+  if (a.casc_width > 0) {
+    err = launch_share(a, s);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "shared-prefix detection launch failed: %s", hipGetErrorString(err));
+  }
+  err = launch_decode(a, dtype, head_dim, p.grid, p.lds, s);
   if (err != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
   if (opts && opts->event_end) {
     err = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->event_end), s);

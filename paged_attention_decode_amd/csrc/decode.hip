@@ -47,10 +47,14 @@ struct Piece {
   // Runs tiles [lt0, lt1) of segment (s, r). complete: the piece is the whole
   // segment, so the normalised result goes straight to `out`; otherwise to
   // part_o / part_lse (rows of the group's heads, in LDS) when given, else to
-  // workspace slot `slot` of range `rng`.
+  // workspace rows row_base + column.
+  // cols != 0: a shared prefix. The tiles are read through sequence s's block table, and the
+  // columns are the kv head's query heads of the sequences win + m for each bit m of cols
+  // (column m * group + head); the result always goes to the workspace, all 16 columns.
   static __device__ __forceinline__ void run(const DecodeArgs& a, int s, int r, int L, int lt0, int lt1,
-                                             bool complete, int rng, int slot, int lane,
-                                             float* part_o = nullptr, float* part_lse = nullptr) {
+                                             bool complete, int64_t row_base, int lane,
+                                             float* part_o = nullptr, float* part_lse = nullptr,
+                                             int win = 0, int cols = 0) {
     // All of these are the same in every lane. Saying so lets the compiler keep what derives
     // from them in scalar registers, and read the block table with scalar loads.
     s = __builtin_amdgcn_readfirstlane(s);
@@ -58,6 +62,8 @@ struct Piece {
     L = __builtin_amdgcn_readfirstlane(L);
     lt0 = __builtin_amdgcn_readfirstlane(lt0);
     lt1 = __builtin_amdgcn_readfirstlane(lt1);
+    win = __builtin_amdgcn_readfirstlane(win);
+    cols = __builtin_amdgcn_readfirstlane(cols);
     const int kq = lane >> 4;  // operand k-group, and result row group
     const int ln = lane & 15;  // operand row, and result column (= head in group)
     const int g = r / a.n_hg;
@@ -65,15 +71,33 @@ struct Piece {
     const int h0 = g * a.group + hg * kHeadsPerTile;
     const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
     const int bs = a.block_size;
+    const bool shared = cols != 0;
 
-    // Query operand: Q[h0 + ln][16-byte chunk 4j + kq]. The resource covers the group's gh
-    // head rows only, so padding columns (ln >= gh) read zeros, with no branch around the loads.
+    // Query operand: row of column ln, 16-byte chunk 4j + kq. The resource covers the column
+    // rows only, and a padding column's offset lies past its end, so padding columns read zeros
+    // with no branch around the loads.
+    bool valid;
     u4 qv[C::kLoads];
     {
-      const char* qg = reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.q_seq_stride + (int64_t)h0 * D) * C::kE;
-      const __amdgpu_buffer_rsrc_t qr = page_rsrc(qg, gh * D * C::kE);
+      const char* qg;
+      int qbytes, qoff;
+      if (shared) {
+        const int m = ln / a.group;
+        const int hl = ln - m * a.group;
+        valid = ((cols >> m) & 1) != 0;
+        const int rows = min(a.casc_width, a.num_seqs - win);
+        qg = reinterpret_cast<const char*>(a.q) + ((int64_t)win * a.q_seq_stride + (int64_t)g * a.group * D) * C::kE;
+        qbytes = (int)(((int64_t)(rows - 1) * a.q_seq_stride + (int64_t)a.group * D) * C::kE);
+        qoff = valid ? (int)(((int64_t)m * a.q_seq_stride + (int64_t)hl * D) * C::kE) : qbytes;
+      } else {
+        valid = ln < gh;
+        qg = reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.q_seq_stride + (int64_t)h0 * D) * C::kE;
+        qbytes = gh * D * C::kE;
+        qoff = ln * D * C::kE;
+      }
+      const __amdgpu_buffer_rsrc_t qr = page_rsrc(qg, qbytes);
 #pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) qv[j] = buf_load16<kPolicyDefault>(qr, ln * D * C::kE + (4 * j + kq) * 16);
+      for (int j = 0; j < C::kLoads; ++j) qv[j] = buf_load16<kPolicyDefault>(qr, qoff + (4 * j + kq) * 16);
     }
 
     f4 acc[C::kAcc];
@@ -108,7 +132,7 @@ struct Piece {
       // writes them to the token's cache slot.
       const int tl = (L - 1) >> 4;
       const int r0 = (L - 1) & (kTile - 1);
-      const bool fuse = FUSE && tl >= lt0 && tl < lt1;
+      const bool fuse = FUSE && !shared && tl >= lt0 && tl < lt1;
       u4 knew[C::kLoads];           // key chunk 4j + kq (used by the lanes of row r0)
       uint32_t vnew[C::kLoads];     // value dims 32w + 2ln, +1 (16-bit) or dim 16u + ln (fp32)
       int64_t blk_new = 0;
@@ -337,7 +361,7 @@ struct Piece {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = (L > 0) ? 1.0f / lt : 0.0f;
-    if (ln >= gh) return;
+    if (!valid) return;
 
     float* dst_f32 = nullptr;
     void* dst = a.out;
@@ -351,7 +375,7 @@ struct Piece {
       as_f32 = true;
       if (kq == 0) part_lse[ln] = m + __log2f(lt);
     } else {
-      const int64_t row = ((int64_t)rng * 2 + slot) * a.gh_max + ln;
+      const int64_t row = row_base + ln;
       dst_f32 = a.ws_o;
       dst = dst_f32;
       base = row * D;
@@ -423,12 +447,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       const int tiles = max(1, (L + kTile - 1) / kTile);
       const int parts = min(kWavesPerGroup, tiles);
       if (parts == 1) {
-        if (wv == 0) Piece<DT, D, FUSE>::run(a, s, r, L, 0, tiles, true, 0, 0, lane);
+        if (wv == 0) Piece<DT, D, FUSE>::run(a, s, r, L, 0, tiles, true, 0, lane);
         continue;
       }
       // Every share is non-empty and starts below L, so every partial has a finite lse.
       if (wv < parts)
-        Piece<DT, D, FUSE>::run(a, s, r, L, wv * tiles / parts, (wv + 1) * tiles / parts, false, 0, 0, lane,
+        Piece<DT, D, FUSE>::run(a, s, r, L, wv * tiles / parts, (wv + 1) * tiles / parts, false, 0, lane,
                                 part_o + wv * a.gh_max * D, part_lse + wv * a.gh_max);
       __syncthreads();
       const int g = r / a.n_hg;
@@ -471,20 +495,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       const int r = seg - s * H;
       const int L = clamp_len(a.context_lens[s], max_len);
       const int tiles = max(1, (L + kTile - 1) / kTile);
-      Piece<DT, D, FUSE>::run(a, s, r, L, 0, tiles, true, wave, 0, lane);
+      Piece<DT, D, FUSE>::run(a, s, r, L, 0, tiles, true, 0, lane);
     }
     return;
   }
 
   // Prefix sums of tiles per sequence (every segment has at least one tile,
   // so an empty sequence still gets a wavefront that writes its zeros).
+  // Shared prefixes: a sequence in a group reads only the tiles after the group's prefix, and
+  // the group's leader also owns the prefix segments (one per kv head), ahead of its own.
+  const int CW = a.casc_width;
+  int32_t* s_share = s_prefix + a.num_seqs + 1;  // [num_seqs] sharing words (CW > 0)
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += kDecodeThreads) {
     const int i = base + tid;
     int v = 0;
     if (i < a.num_seqs) {
       const int L = clamp_len(a.context_lens[i], max_len);
-      v = max(1, (L + kTile - 1) / kTile) * H;
+      int tiles = max(1, (L + kTile - 1) / kTile);
+      if (CW > 0) {
+        const int w = a.ws_share[i];
+        s_share[i] = w;
+        if (w & kShareIncluded) {
+          const int pt = share_tiles(w);
+          tiles -= (i % CW == share_leader(w)) ? 0 : pt;
+        }
+      }
+      v = tiles * H;
     }
     int x = v;
 #pragma unroll
@@ -531,33 +568,168 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       if (s_prefix[mid] <= t) lo = mid; else hi = mid;
     }
     int s = lo;
-    int L = clamp_len(a.context_lens[s], max_len);
-    int tiles = max(1, (L + kTile - 1) / kTile);
-    const int local = t - s_prefix[s];
-    int r = local / tiles;
-    int lt = local - r * tiles;
+    // Sequence s's segments, in tile order: pre_tiles-tile prefix segments r = 0..H-1 (a group
+    // leader only), then its own segments r = 0..H-1, tiles [skip, skip + own) of the context.
+    int L, pre_tiles, skip, own, word;
+    auto enter = [&]() {
+      L = clamp_len(a.context_lens[s], max_len);
+      word = CW > 0 ? s_share[s] : 0;
+      skip = (word & kShareIncluded) ? share_tiles(word) : 0;
+      pre_tiles = ((word & kShareIncluded) && s % CW == share_leader(word)) ? skip : 0;
+      own = max(1, (L + kTile - 1) / kTile - skip);
+    };
+    enter();
+    int local = t - s_prefix[s];
+    bool in_pre = local < H * pre_tiles;
+    if (!in_pre) local -= H * pre_tiles;
+    int r = local / (in_pre ? pre_tiles : own);
+    int lt = local - r * (in_pre ? pre_tiles : own);
     bool first = true;
     while (true) {
+      const int tiles = in_pre ? pre_tiles : own;
       const int n = min(tiles - lt, t_end - t);
-      const bool complete = (lt == 0) && (n == tiles);
       const int slot = first ? 0 : 1;
+      // A piece cut by a range boundary is the range's first (slot 0) or last (slot 1). A whole
+      // segment is finished here, unless it belongs to a shared-prefix group (a prefix segment,
+      // or a member's own tiles): the merge adds the prefix's partials, so it leaves one partial
+      // in rows of its own.
+      const bool whole = lt == 0 && n == tiles;
+      const bool complete = whole && !in_pre && word == 0;
+      int64_t row_base = ((int64_t)rho * 2 + slot) * a.ws_cols;
+      if (whole && in_pre) row_base = a.whole_pre_row + ((int64_t)(s / CW) * H + r) * kHeadsPerTile;
+      else if (whole) row_base = a.whole_own_row + ((int64_t)s * H + r) * a.gh_max;
       if (lt == 0 && lane == 0) {
         // This range holds the segment's first piece: record where all pieces are.
-        a.ws_meta[(int64_t)s * H + r] = make_int4(rho, slot, (t + tiles - 1) / R, 0);
+        int4* meta = in_pre ? a.ws_meta_pre + (int64_t)(s / CW) * H + r : a.ws_meta + (int64_t)s * H + r;
+        *meta = make_int4(rho, slot, (t + tiles - 1) / R, 0);
       }
-      Piece<DT, D, FUSE>::run(a, s, r, L, lt, lt + n, complete, rho, slot, lane);
+      int win = 0, cols = 0, p_len = L, p_lt0 = skip + lt;
+      if (in_pre) {
+        // The window's group members: the sequences whose word marks them included.
+        win = s - s % CW;
+        for (int m = 0; m < CW && win + m < a.num_seqs; ++m)
+          cols |= ((s_share[win + m] & kShareIncluded) ? 1 : 0) << m;
+        p_len = pre_tiles * kTile;
+        p_lt0 = lt;
+      }
+      Piece<DT, D, FUSE>::run(a, s, r, p_len, p_lt0, p_lt0 + n, complete, row_base, lane, nullptr, nullptr,
+                              win, cols);
       t += n;
       if (t >= t_end) break;
       first = false;
       lt = 0;
       if (++r == H) {
         r = 0;
-        ++s;
-        L = clamp_len(a.context_lens[s], max_len);
-        tiles = max(1, (L + kTile - 1) / kTile);
+        if (in_pre) {
+          in_pre = false;
+        } else {
+          ++s;
+          enter();
+          in_pre = pre_tiles > 0;
+        }
       }
     }
   }
+}
+
+// Shared-prefix detection. Sequences are taken in windows of CW = casc_width consecutive ones
+// (CW = 16 / group: the query heads of one kv head of CW sequences fill the 16 columns of a
+// matrix-core tile); one workgroup of CW wavefronts per window.
+// - A sequence takes part if it has a whole block before the block of its last token (the
+//   block holding the last token is the one a decode step writes, so it is never shared).
+// - The candidates are the sequences whose first physical block is the window's most common
+//   one; the first of them leads.
+// - Candidate m shares the leading blocks whose physical ids equal the leader's, counted over
+//   the whole blocks before either one's last-token block. Ids are compared as the attention
+//   kernel uses them (clamped into the pool), so equal ids mean the same K/V bytes.
+// - The prefix is the P blocks that maximise P times the number of non-leader candidates
+//   sharing at least P blocks: the reads that reading them once saves. The leader and those
+//   candidates form the group, if the prefix is at least two tiles long.
+// One word per window sequence: kShareIncluded | leader slot << 16 | prefix tiles, 0 if not in
+// the group.
+__global__ __launch_bounds__(1024) void share_kernel(const DecodeArgs a) {
+  __shared__ int s_blocks[kHeadsPerTile];
+  const int CW = a.casc_width;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;  // the window slot this wavefront compares
+  const int s0 = blockIdx.x * CW;
+  const int n = min(CW, a.num_seqs - s0);
+  const int max_len = a.max_blocks << a.bs_log2;
+  const int64_t nb_max = a.num_blocks - 1;
+  auto blk = [&](int v) -> int { return v < 0 ? 0 : ((int64_t)v > nb_max ? (int)nb_max : v); };
+  // Lanes 0..n-1 hold the window's sequences (in every wavefront).
+  const int me = min(lane, n - 1);
+  const int L = clamp_len(a.context_lens[s0 + me], max_len);
+  const int cap = (lane < n && L > 0) ? ((L - 1) >> a.bs_log2) : 0;
+  const int first = blk(a.block_tables[(int64_t)(s0 + me) * a.max_blocks]);
+  int cnt = 0;
+  for (int j = 0; j < n; ++j) {
+    const int fj = __shfl(first, j), cj = __shfl(cap, j);
+    cnt += (cj > 0 && fj == first) ? 1 : 0;
+  }
+  // Most candidates, then lowest slot.
+  int key = cap > 0 ? cnt * 64 + (63 - lane) : -1;
+  for (int off = 32; off >= 1; off >>= 1) key = max(key, __shfl_xor(key, off));
+  const int leader = 63 - (key & 63);
+  const bool group = key >= 2 * 64;
+  const int first_l = __shfl(first, leader), cap_l = __shfl(cap, leader);
+
+  int shared_blocks = 0;
+  if (group && wv < n) {
+    const int first_m = __shfl(first, wv), cap_m = __shfl(cap, wv);
+    if (wv == leader) {
+      shared_blocks = cap_l;
+    } else if (cap_m > 0 && first_m == first_l) {
+      const int lim = min(cap_m, cap_l);  // >= 1, and < max_blocks: every index below is in the row
+      const int32_t* rm = a.block_tables + (int64_t)(s0 + wv) * a.max_blocks;
+      const int32_t* rl = a.block_tables + (int64_t)(s0 + leader) * a.max_blocks;
+      shared_blocks = lim;
+      for (int j0 = 0; j0 < lim; j0 += 256) {
+        int x[4], y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = min(j0 + 64 * k + lane, lim - 1);
+          x[k] = blk(rm[j]);
+          y[k] = blk(rl[j]);
+        }
+        int found = -1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = j0 + 64 * k + lane;
+          const unsigned long long bad = __ballot(j < lim && x[k] != y[k]);
+          if (found < 0 && bad != 0) found = j0 + 64 * k + __builtin_ctzll(bad);
+        }
+        if (found >= 0) {
+          shared_blocks = found;
+          break;
+        }
+      }
+    }
+  }
+  if (lane == 0 && wv < kHeadsPerTile) s_blocks[wv] = shared_blocks;
+  __syncthreads();
+  if (wv != 0) return;
+
+  const int sh = lane < n ? s_blocks[lane] : 0;
+  // Saving of a prefix of sh blocks: sh times the non-leader candidates that share that many.
+  int c = 0;
+  for (int j = 0; j < n; ++j) {
+    const int shj = __shfl(sh, j);
+    c += (j != leader && shj > 0 && shj >= sh) ? 1 : 0;
+  }
+  const bool cand = group && lane < n && lane != leader && sh > 0;
+  const int saving = cand ? c * sh : 0;  // <= 15 * max_blocks, no overflow
+  int best = saving;
+  for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off));
+  // The lowest slot with the best saving gives the prefix length.
+  const unsigned long long at = __ballot(cand && saving == best);
+  const int tiles_per_block = a.block_size / kTile;
+  int p_blocks = (best > 0 && at != 0) ? __shfl(sh, (int)__builtin_ctzll(at)) : 0;
+  p_blocks = min(p_blocks, 0xFFFF / tiles_per_block);
+  const int p_tiles = p_blocks * tiles_per_block;
+  const bool ok = p_tiles >= 2;
+  const bool inc = ok && lane < n && (lane == leader || sh >= p_blocks);
+  if (lane < n) a.ws_share[s0 + lane] = inc ? (kShareIncluded | (leader << 16) | p_tiles) : 0;
 }
 
 // Fused decode step, split modes: cache write of sequence s's new token (position L-1) for kv
@@ -611,14 +783,34 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   const int hg = r - g * a.n_hg;
   const int gh = min(kHeadsPerTile, a.group - hg * kHeadsPerTile);
   if (n >= gh) return;
-  if (a.k_new != nullptr && n == 0 && hg == 0) store_new_token<DT, D>(a, seg / a.segs_per_seq, g, lane);
+  const int s = seg / a.segs_per_seq;
+  if (a.k_new != nullptr && n == 0 && hg == 0) store_new_token<DT, D>(a, s, g, lane);
   const int4 meta = a.ws_meta[seg];
   const int wa = meta.x, slot_a = meta.y, wb = meta.z;
-  if (wb <= wa) return;  // finished inside one range
-  const int np = wb - wa + 1;
-  // Workspace row of piece p: range wa + p, slot slot_a for the first piece, 0 after it.
+  // A sequence in a shared-prefix group also has the pieces of its window's prefix segment,
+  // in column (window slot) * group + n.
+  int pa = 0, slot_p = 0, np_pre = 0, col_p = 0;
+  if (a.casc_width > 0 && (a.ws_share[s] & kShareIncluded)) {
+    const int4 pm = a.ws_meta_pre[(int64_t)(s / a.casc_width) * a.segs_per_seq + r];
+    pa = pm.x;
+    slot_p = pm.y;
+    np_pre = pm.z - pm.x + 1;
+    col_p = (s % a.casc_width) * a.group + n;
+  }
+  if (wb <= wa && np_pre == 0) return;  // finished inside one range
+  const int np_own = wb - wa + 1;
+  const int np = np_own + np_pre;
+  // Workspace row of piece p: own pieces first (range wa + p, slot slot_a for the first piece,
+  // 0 after it), then the prefix's. A segment left whole in one range has rows of its own.
   auto row_of = [&](int p) -> int64_t {
-    return ((int64_t)(wa + p) * 2 + (p == 0 ? slot_a : 0)) * a.gh_max + n;
+    if (p < np_own) {
+      if (np_own == 1) return a.whole_own_row + (int64_t)seg * a.gh_max + n;
+      return ((int64_t)(wa + p) * 2 + (p == 0 ? slot_a : 0)) * a.ws_cols + n;
+    }
+    const int q = p - np_own;
+    if (np_pre == 1)
+      return a.whole_pre_row + ((int64_t)(s / a.casc_width) * a.segs_per_seq + r) * kHeadsPerTile + col_p;
+    return ((int64_t)(pa + q) * 2 + (q == 0 ? slot_p : 0)) * a.ws_cols + col_p;
   };
   // Pieces 0..63's lse and the first kBatch pieces' rows are loaded together: the rows do not
   // depend on the weights, so the merge waits for memory once before its first products.
@@ -663,7 +855,6 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   const float inv = 1.0f / wsum;
-  const int s = seg / a.segs_per_seq;
   const int h0 = g * a.group + hg * kHeadsPerTile;
   const int64_t obase = ((int64_t)s * a.num_heads + h0 + n) * D + lane * kPer;
 #pragma unroll
@@ -695,6 +886,12 @@ hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_share_t(const DecodeArgs& a, hipStream_t st) {
+  const int windows = (a.num_seqs + a.casc_width - 1) / a.casc_width;
+  hipLaunchKernelGGL(share_kernel, dim3(windows), dim3(64 * a.casc_width), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t occupancy_t(size_t lds, int* groups) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups, decode_kernel<DT, D, false>, kDecodeThreads, lds);
@@ -722,6 +919,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid,
   }
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_share(const DecodeArgs& a, hipStream_t st) { return launch_share_t(a, st); }
 
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st) {
   switch (dtype) {

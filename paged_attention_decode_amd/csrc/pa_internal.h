@@ -19,6 +19,14 @@ constexpr int kWavesPerGroup = kDecodeThreads / 64;
 constexpr int kHeadsPerTile = 16;
 // Largest batch: per-sequence tile prefix sums live in LDS (4 bytes each).
 constexpr int kMaxSeqs = 16383;
+// Largest batch for shared-prefix decode: the per-sequence sharing words also live in LDS.
+constexpr int kMaxSharedSeqs = 8191;
+// Shared-prefix word of a sequence (0: the sequence reads its whole context itself):
+// bits 0-15 the prefix length in 16-token tiles, bits 16-19 the window slot of the group's
+// leader (whose block table the prefix is read through), bit 20 set.
+constexpr int kShareIncluded = 1 << 20;
+__host__ __device__ inline int share_tiles(int w) { return w & 0xFFFF; }
+__host__ __device__ inline int share_leader(int w) { return (w >> 16) & 15; }
 // partition_size (and DecodeArgs::range_tiles) of the workgroup-split mode: the wavefronts of a
 // workgroup share one segment's tiles and merge their partial results in LDS.
 constexpr int kWorkgroupSplit = -3;
@@ -35,9 +43,19 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_o;        // [num_waves][2][gh_max][head_dim] normalised partial outputs
-  float* ws_lse;      // [num_waves][2][gh_max] log2-sum-exp2 of each partial
-  int4* ws_meta;      // [num_seqs * segs_per_seq] {first wave, its slot, last wave, 0}
+  // Normalised partial outputs, one row of head_dim floats each, and their log2-sum-exp2:
+  // rows [ranges][2][ws_cols] for pieces cut by range boundaries, then (shared prefixes only)
+  // whole_own_row.. [num_seqs * segs_per_seq][gh_max] and whole_pre_row..
+  // [windows * segs_per_seq][16] for whole segments that are still merged.
+  float* ws_o;
+  float* ws_lse;
+  int64_t whole_own_row;
+  int64_t whole_pre_row;
+  int4* ws_meta;      // [num_seqs * segs_per_seq] {first range, its slot, last range, 0}
+  // Shared prefixes (casc_width > 0): per-sequence words written by the detection kernel, and
+  // the pieces of each window's prefix segments, [ceil(num_seqs / casc_width) * segs_per_seq].
+  int32_t* ws_share;
+  int4* ws_meta_pre;
   int64_t q_seq_stride;   // elements
   int64_t num_blocks;
   float scale_log2;       // scale * log2(e)
@@ -55,6 +73,8 @@ struct DecodeArgs {
   int32_t num_waves;      // wavefronts launched
   int32_t range_tiles;    // >0 fixed tiles per wavefront, 0 balanced, -1 one pass, kWorkgroupSplit
   int32_t cached_prefix_tokens;  // tiles starting before this token use cached loads, later ones stream
+  int32_t ws_cols;        // partial-output columns per (range, slot): gh_max, or 16 with shared prefixes
+  int32_t casc_width;     // sequences per shared-prefix window (16 / group), 0 = no prefix sharing
   // Fused scatter of the step's token at position L-1 (null: plain decode).
   const void* k_new;      // [num_seqs][num_kv_heads][head_dim]
   const void* v_new;
@@ -115,6 +135,8 @@ hipError_t launch_prefill_shared(const PrefillArgs& a, int dtype, int head_dim, 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
                          hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// Shared-prefix detection: fills a.ws_share (one workgroup per window of a.casc_width sequences).
+hipError_t launch_share(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
                               int32_t num_pairs, int64_t block_bytes, int64_t num_blocks, hipStream_t stream);

@@ -221,3 +221,30 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         pa.paged_attention_decode(torch.zeros(1, 1, 64, dtype=torch.float16), k, v,
                                   torch.zeros(1, 2, dtype=torch.int32), torch.ones(1, dtype=torch.int32), 0.1)
+
+
+def test_plan_shared_prefix_window_and_workspace():
+    # G = 2: windows of 8 sequences; partial rows get 16 columns, plus prefix records and words
+    base = _plan(partition_size=-2)
+    sp = _plan(partition_size=-2, shared_prefix=True)
+    assert base["shared_prefix_window"] == 0 and sp["shared_prefix_window"] == 8
+    rows = sp["num_waves"] * 2 * 16
+    assert sp["workspace_bytes"] >= rows * 128 * 4 + rows * 4 + 256 * 8 * 16 + 32 * 8 * 16 + 256 * 4
+    assert sp["workspace_bytes"] > base["workspace_bytes"]
+    assert sp["num_waves"] == base["num_waves"] and sp["range_tokens"] == base["range_tokens"]
+    # windows of 16 // G sequences for every G up to 8
+    for g, w in ((1, 16), (3, 5), (4, 4), (5, 3), (8, 2)):
+        assert _plan(num_heads=2 * g, num_kv_heads=2, partition_size=512, shared_prefix=True)[
+            "shared_prefix_window"] == w
+
+
+@pytest.mark.parametrize("kw", [dict(partition_size=-1), dict(partition_size=-3), dict(num_heads=32, num_kv_heads=2),
+                                dict(num_heads=40, num_kv_heads=2), dict(num_seqs=8192),
+                                dict(max_blocks_per_seq=16)])  # automatic mode picks one pass at 256 tokens
+def test_plan_shared_prefix_does_not_apply(kw):
+    args = dict(shared_prefix=True)
+    args.update(kw)
+    p = _plan(**args)
+    assert p["shared_prefix_window"] == 0
+    args["shared_prefix"] = False
+    assert p["workspace_bytes"] == _plan(**args)["workspace_bytes"]

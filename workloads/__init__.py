@@ -6,5 +6,5 @@ and holds none of the attention arithmetic. Caches are returned as flat arrays
 of i.i.d. values; each consumer applies its own view of the physical layout.
 """
 
-from .configs import CONFIGS, CONFIG_ORDER, Config, get_config  # noqa: F401
+from .configs import CONFIGS, CONFIG_ORDER, EXTRA_CONFIGS, Config, get_config  # noqa: F401
 from .gen import Inputs, make_inputs, nan_of, poison_blocks, to_storage  # noqa: F401

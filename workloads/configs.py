@@ -85,9 +85,17 @@ CONFIGS = {
 CONFIG_ORDER = ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16", "long_ctx_bf16",
                 "skewed_prefix_bf16"]
 
+# A further prefix-caching shape, for the shared-prefix option: 32 prompts of 4096 tokens, each
+# sampled 8 times (groups of 8 sequences share the prompt's blocks), 1 to 512 tokens generated
+# per sample. The distinct prompt K/V (0.54 GB) is larger than the 256 MB last-level cache.
+CONFIGS["shared_prompt_bf16"] = Config(
+    name="shared_prompt_bf16", dtype="bf16", batch=256, num_heads=16, num_kv_heads=8, head_dim=128,
+    block_size=16, lengths="uniform", len_lo=4097, len_hi=4608, prefix_group=8, prefix_tokens=4096, seed=6)
+EXTRA_CONFIGS = ["shared_prompt_bf16"]
+
 
 def get_config(name: str) -> Config:
     try:
         return CONFIGS[name]
     except KeyError:
-        raise KeyError(f"unknown workload {name!r}; known: {CONFIG_ORDER}") from None
+        raise KeyError(f"unknown workload {name!r}; known: {CONFIG_ORDER + EXTRA_CONFIGS}") from None
