@@ -406,7 +406,9 @@ struct Piece {
 #define PA_XCD_REMAP 1
 #endif
 
-template <int DT, int D, bool FUSE>
+// SHARED: the call reads shared prefixes (split modes only); a separate instance keeps that
+// bookkeeping out of the plain kernel's walk over its ranges.
+template <int DT, int D, bool FUSE, bool SHARED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   // Split modes: [num_seqs + 1], the first global tile of each sequence. Workgroup split: the
   // partial rows of the segment being merged.
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   // so an empty sequence still gets a wavefront that writes its zeros).
   // Shared prefixes: a sequence in a group reads only the tiles after the group's prefix, and
   // the group's leader also owns the prefix segments (one per kv head), ahead of its own.
-  const int CW = a.casc_width;
+  const int CW = SHARED ? a.casc_width : 0;
   int32_t* s_share = s_prefix + a.num_seqs + 1;  // [num_seqs] sharing words (CW > 0)
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += kDecodeThreads) {
@@ -768,8 +770,10 @@ __device__ __forceinline__ void store_new_token(const DecodeArgs& a, int s, int 
 // Merge of the pieces of every cut segment: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),
 // M = max_p lse_p. One wavefront per (segment, head): lane p holds piece p's lse, the pieces'
 // output rows are read eight at a time so their loads are in flight together. Summation order
-// is fixed (deterministic).
-template <int DT, int D>
+// is fixed (deterministic). SHARED: the call reads shared prefixes, so a sequence in a group also
+// merges its window's prefix pieces; a separate instance keeps that bookkeeping out of the
+// plain merge.
+template <int DT, int D, bool SHARED>
 __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   constexpr int kPer = D / 64;
   constexpr int kBatch = 8;
@@ -790,27 +794,37 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   // A sequence in a shared-prefix group also has the pieces of its window's prefix segment,
   // in column (window slot) * group + n.
   int pa = 0, slot_p = 0, np_pre = 0, col_p = 0;
-  if (a.casc_width > 0 && (a.ws_share[s] & kShareIncluded)) {
-    const int4 pm = a.ws_meta_pre[(int64_t)(s / a.casc_width) * a.segs_per_seq + r];
-    pa = pm.x;
-    slot_p = pm.y;
-    np_pre = pm.z - pm.x + 1;
-    col_p = (s % a.casc_width) * a.group + n;
+  if constexpr (SHARED) {
+    if (a.ws_share[s] & kShareIncluded) {
+      const int4 pm = a.ws_meta_pre[(int64_t)(s / a.casc_width) * a.segs_per_seq + r];
+      pa = pm.x;
+      slot_p = pm.y;
+      np_pre = pm.z - pm.x + 1;
+      col_p = (s % a.casc_width) * a.group + n;
+    }
   }
   if (wb <= wa && np_pre == 0) return;  // finished inside one range
   const int np_own = wb - wa + 1;
   const int np = np_own + np_pre;
-  // Workspace row of piece p: own pieces first (range wa + p, slot slot_a for the first piece,
-  // 0 after it), then the prefix's. A segment left whole in one range has rows of its own.
+  // Workspace row of piece p: range wa + p, slot slot_a for the first piece, 0 after it. With
+  // shared prefixes the prefix's pieces follow the own ones, and a segment left whole in one
+  // range has rows of its own. Selects only: a lane-dependent branch here would split the
+  // batched loads below.
+  const int64_t own_whole = a.whole_own_row + (int64_t)seg * a.gh_max + n;
+  const int64_t pre_whole =
+      np_pre > 0 ? a.whole_pre_row + ((int64_t)(s / a.casc_width) * a.segs_per_seq + r) * kHeadsPerTile + col_p : 0;
   auto row_of = [&](int p) -> int64_t {
-    if (p < np_own) {
-      if (np_own == 1) return a.whole_own_row + (int64_t)seg * a.gh_max + n;
+    if constexpr (!SHARED) {
       return ((int64_t)(wa + p) * 2 + (p == 0 ? slot_a : 0)) * a.ws_cols + n;
+    } else {
+      const bool own = p < np_own;
+      const int q = own ? p : p - np_own;
+      const int first_slot = own ? slot_a : slot_p;
+      const int64_t cut =
+          ((int64_t)((own ? wa : pa) + q) * 2 + (q == 0 ? first_slot : 0)) * a.ws_cols + (own ? n : col_p);
+      const bool whole = own ? np_own == 1 : np_pre == 1;
+      return whole ? (own ? own_whole : pre_whole) : cut;
     }
-    const int q = p - np_own;
-    if (np_pre == 1)
-      return a.whole_pre_row + ((int64_t)(s / a.casc_width) * a.segs_per_seq + r) * kHeadsPerTile + col_p;
-    return ((int64_t)(pa + q) * 2 + (q == 0 ? slot_p : 0)) * a.ws_cols + col_p;
   };
   // Pieces 0..63's lse and the first kBatch pieces' rows are loaded together: the rows do not
   // depend on the weights, so the merge waits for memory once before its first products.
@@ -872,17 +886,28 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
 
 template <int DT, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
-  if (a.k_new != nullptr)
-    hipLaunchKernelGGL((decode_kernel<DT, D, true>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<DT, D, false>), dim3(grid), dim3(kDecodeThreads), lds, st, a);
+  const dim3 g(grid), b(kDecodeThreads);
+  if (a.casc_width > 0) {
+    if (a.k_new != nullptr)
+      hipLaunchKernelGGL((decode_kernel<DT, D, true, true>), g, b, lds, st, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<DT, D, false, true>), g, b, lds, st, a);
+  } else if (a.k_new != nullptr) {
+    hipLaunchKernelGGL((decode_kernel<DT, D, true, false>), g, b, lds, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<DT, D, false, false>), g, b, lds, st, a);
+  }
   return hipGetLastError();
 }
 
 template <int DT, int D>
 hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.num_seqs * a.segs_per_seq * a.gh_max;
-  hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((items + 3) / 4));
+  if (a.casc_width > 0)
+    hipLaunchKernelGGL((reduce_kernel<DT, D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<DT, D, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -894,7 +919,7 @@ hipError_t launch_share_t(const DecodeArgs& a, hipStream_t st) {
 
 template <int DT, int D>
 hipError_t occupancy_t(size_t lds, int* groups) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups, decode_kernel<DT, D, false>, kDecodeThreads, lds);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups, decode_kernel<DT, D, false, false>, kDecodeThreads, lds);
 }
 
 }  // namespace
