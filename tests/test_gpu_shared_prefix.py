@@ -260,3 +260,56 @@ def test_shared_prompt_workload(cuda):
     assert np.abs(out[seqs] - ref[seqs]).max() <= TOL["bf16"]
     del dev
     torch.cuda.empty_cache()
+
+
+def test_graph_capture_with_shared_prefix(cuda):
+    """Store + decode with the option, recorded into a HIP graph (detection, attention and merge
+    kernels): every replay, with eager work between replays, matches the eager step bit for bit,
+    and a changed block table is picked up by the detection on replay."""
+    import torch
+    import paged_attention_decode_amd as pa
+    rng = np.random.default_rng(12)
+    lens = tuple(int(v) for v in rng.integers(40, 600, 16))
+    cfg = custom_config(dtype="bf16", batch=16, hq=8, hkv=4, d=128, bs=16, lens=lens, seed=13, prefix_group=8,
+                        prefix_tokens=256)
+    x = make_inputs(cfg)
+    c = x.cfg
+    dev = to_device(x, cuda)
+    need = pa.decode_plan(c.batch, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks_per_seq,
+                          pa.DTYPE_BF16, -2, 0, shared_prefix=True)["workspace_bytes"]
+    ws = torch.empty(need, dtype=torch.uint8, device=cuda)
+    out = torch.empty((c.batch, c.num_heads, c.head_dim), dtype=torch.float32, device=cuda)
+
+    def step():
+        pa.store_kvcache(dev["k_new"], dev["v_new"], dev["slot_mapping"], dev["k_cache"], dev["v_cache"])
+        pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                  dev["context_lens"], x.scale, out, workspace=ws, partition_size=-2,
+                                  shared_prefix=True)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xA5)                   # the workspace needs no initialisation
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes() == eager.cpu().numpy().tobytes(), f"replay {rep}"
+    _, _, ref = oracle_after_store(x)
+    assert np.abs(eager.cpu().numpy() - ref).max() <= TOL["bf16"]
+    # break the sharing of most of the second window in place (their first block becomes their own
+    # last block): a replay must regroup
+    tables = x.block_tables.copy()
+    for m in range(9, 16):
+        tables[m, 0] = tables[m, (int(x.context_lens[m]) - 1) // 16]
+    dev["block_tables"].copy_(torch.from_numpy(tables))
+    x2 = x
+    x2.block_tables = tables
+    g.replay()
+    torch.cuda.synchronize()
+    _, _, ref2 = oracle_after_store(x2)
+    assert np.abs(out.cpu().numpy() - ref2).max() <= TOL["bf16"]
