@@ -3,11 +3,13 @@
 // cache management). Bit copies, no conversion.
 //
 // One thread per (token, kv head, 16-byte chunk of the row). The K chunk maps
-// to one 16-byte run of the K page (layout [.. D/x][bs][x]); the V chunk's x
-// elements go to x separate dims of the V page (layout [.. bs/4][D][4]), each
-// at the token's position inside its group of four.
+// to one 16-byte run of the K page (layout [.. D/x][bs][x]). Each thread also
+// moves x value elements of the token to x dims of the V page (layout
+// [.. bs/4][D][4]), each at the token's position inside its group of four.
 
 #include "pa_internal.h"
+
+#include <type_traits>
 
 namespace pa {
 namespace {
@@ -32,28 +34,26 @@ __global__ __launch_bounds__(256) void store_kernel(const StoreArgs a) {
   const int64_t page = (blk * a.num_kv_heads + g) * (int64_t)a.block_size * a.head_dim;  // elements
 
   const char* ksrc = reinterpret_cast<const char*>(a.k) + ((int64_t)i * a.k_stride + (int64_t)g * a.head_dim + (int64_t)c * kX) * E;
-  const char* vsrc = reinterpret_cast<const char*>(a.v) + ((int64_t)i * a.v_stride + (int64_t)g * a.head_dim + (int64_t)c * kX) * E;
   const u4 kv = *reinterpret_cast<const u4*>(ksrc);
-  const u4 vv = *reinterpret_cast<const u4*>(vsrc);
+  // V: in step j, lane c of a (token, head) takes dim j * chunks + c. The lanes of one store
+  // then write neighbouring dims, 4 * E bytes apart in the page, and those writes combine into
+  // a few memory requests (with dims c * kX + j each lane's writes would fall in a segment of
+  // its own). Loads first, so that they are in flight together.
+  using VE = typename std::conditional<E == 4, uint32_t, uint16_t>::type;
+  const VE* vsrc = reinterpret_cast<const VE*>(reinterpret_cast<const char*>(a.v) +
+                                               ((int64_t)i * a.v_stride + (int64_t)g * a.head_dim) * E);
+  VE vv[kX];
+#pragma unroll
+  for (int j = 0; j < kX; ++j) vv[j] = vsrc[j * chunks + c];
 
   char* kdst = reinterpret_cast<char*>(a.k_cache) + (page + ((int64_t)c * a.block_size + o) * kX) * E;
   *reinterpret_cast<u4*>(kdst) = kv;
 
   // V element (o, d) sits at [(o / 4) * D + d] * 4 + o % 4 within the page.
-  char* vpage = reinterpret_cast<char*>(a.v_cache) + page * E;
+  VE* vdst = reinterpret_cast<VE*>(reinterpret_cast<char*>(a.v_cache) + page * E);
   const int64_t vrow = (int64_t)(o >> 2) * a.head_dim * 4 + (o & 3);
-  if constexpr (E == 4) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(vpage);
 #pragma unroll
-    for (int j = 0; j < kX; ++j) dst[vrow + (int64_t)(c * kX + j) * 4] = vv[j];
-  } else {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(vpage);
-#pragma unroll
-    for (int j = 0; j < kX; ++j) {
-      const uint32_t w = vv[j >> 1];
-      dst[vrow + (int64_t)(c * kX + j) * 4] = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu));
-    }
-  }
+  for (int j = 0; j < kX; ++j) vdst[vrow + (int64_t)(j * chunks + c) * 4] = vv[j];
 }
 
 // Whole-block copies for copy-on-write: one thread per (pair, 16-byte chunk of a block's
