@@ -15,6 +15,13 @@
 // a segment cut by range boundaries leaves one normalised partial output and
 // its log2-sum-exp2 per piece, merged afterwards by reduce_kernel.
 //
+// Shared prefixes (an option; prefix caching shares the physical blocks of a
+// common prefix between sequences): share_kernel finds, per window of 16/G
+// sequences, a group whose leading block-table entries are the same blocks.
+// The group's prefix then forms segments of its own, whose 16 columns are the
+// group members' heads, read once; each member's own segments start after it,
+// and the merge combines both.
+//
 // Per 16-token tile, one wavefront computes
 //   S[t][h]   = K[t][:] . Q[h][:]          (matrix core: rows = tokens, cols = heads)
 //   online softmax on S (running max m, running sum l, per head = per lane column)
