@@ -2,7 +2,7 @@
 
 Both compare against the oracle on the same seeded inputs.
 - 16383 sequences. This is the largest batch: the split modes keep a per-sequence prefix in LDS,
-  64 KiB at this size.
+  64 KiB at this size. With shared prefixes, 8191 sequences (sharing words beside the prefix).
 - Caches of about 4.3 GiB each. A small case's blocks are relabelled to ids whose byte offsets
   pass 2^32, so the store, decode, prefill and block copy address them with 64-bit offsets. The
   oracle runs on the small case itself; relabelling blocks does not change attention.
@@ -56,6 +56,33 @@ def test_largest_batch_in_every_mode(cuda):
     torch.cuda.synchronize()
     pre = pre.cpu().numpy()
     assert np.abs(pre[seqs] - ref[seqs]).max() <= TOL["bf16"]
+
+
+def test_largest_batch_with_shared_prefixes(cuda):
+    """8191 sequences, the largest batch for shared prefixes (prefix sums and sharing words fill
+    64 KiB of LDS), in groups of 8 sharing their first blocks: sampled rows against the oracle,
+    in the balanced and a fixed mode."""
+    import torch
+    import paged_attention_decode_amd as pa
+    rng = np.random.default_rng(8191)
+    lens = tuple(int(v) for v in rng.integers(1, 100, 8191))
+    x = make_inputs(custom_config(dtype="bf16", batch=len(lens), hq=4, hkv=2, d=128, bs=16, lens=lens, seed=8191,
+                                  prefix_group=8, prefix_tokens=64))
+    dev = to_device(x, cuda)
+    plan = pa.decode_plan(len(lens), 4, 2, 128, 16, x.block_tables.shape[1], pa.DTYPE_BF16, -2, 0,
+                          shared_prefix=True)
+    assert plan["shared_prefix_window"] == 8
+    seqs = list(range(0, len(lens), 97)) + [len(lens) - 1]
+    k2, v2, ref = oracle_after_store(x, seqs=seqs)
+    pa.store_kvcache(dev["k_new"], dev["v_new"], dev["slot_mapping"], dev["k_cache"], dev["v_cache"])
+    for psize in (-2, 64):
+        _say(f"[gpu] 8191 sequences with shared prefixes, partition_size={psize}")
+        out = pa.paged_attention_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                        dev["context_lens"], x.scale, out_dtype=torch.float32, partition_size=psize,
+                                        shared_prefix=True)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        assert np.abs(out[seqs] - ref[seqs]).max() <= TOL["bf16"], psize
 
 
 def test_caches_past_4_gib(cuda):
