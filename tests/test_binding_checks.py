@@ -207,3 +207,20 @@ def test_device_check(devs, ok):
     else:
         with pytest.raises(ValueError):
             pa._require_cuda(*ts)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_options_reach_the_library(lib, shared):
+    """partition_size, cached_prefix_tokens and shared_prefix land in pa_decode_opts for both
+    decode entry points."""
+    a = _decode_args()
+    pa.paged_attention_decode(**a, scale=0.1, partition_size=48, cached_prefix_tokens=-1, shared_prefix=shared)
+    k_new, v_new = torch.zeros(B, HKV, D, dtype=torch.bfloat16), torch.zeros(B, HKV, D, dtype=torch.bfloat16)
+    pa.decode_step(a["q"], k_new, v_new, a["k_cache"], a["v_cache"], a["block_tables"], a["context_lens"], 0.1,
+                   partition_size=-2, shared_prefix=shared)
+    assert [c[0] for c in lib.calls] == ["pa_paged_attention_decode_ex", "pa_decode_step"]
+    o1 = lib.calls[0][1][17]._obj
+    o2 = lib.calls[1][1][21]._obj
+    assert (o1.partition_size, o1.cached_prefix_tokens, o1.shared_prefix) == (48, -1, int(shared))
+    assert (o2.partition_size, o2.shared_prefix) == (-2, int(shared))
+    assert not o1.workspace and not o1.event_begin
