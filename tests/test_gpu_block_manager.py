@@ -16,6 +16,7 @@ import pytest
 import oracle
 from workloads import to_storage
 from _gpu_helpers import np_to_torch
+from test_gpu_shared_prefix import expected_words
 
 pytestmark = pytest.mark.gpu
 
@@ -82,11 +83,25 @@ def test_manager_tables_drive_store_copy_and_decode(cuda):
     lens = np.array([len(seqs[s]) for s in order], np.int32)
     q = to_storage(rng.standard_normal((len(order), HKV * G, D), dtype=np.float32), "bf16")
     scale = 1.0 / np.sqrt(D)
-    for psize in (-3, -2, -1, 0, 16):
+    # the four sequences form one shared-prefix window (G = 4); 1, 2 and 3 share seq 0's leading
+    # blocks (prefix-cache hits and a fork), so the option groups them
+    for psize, shared in ((-3, False), (-2, False), (-1, False), (0, False), (16, False), (-2, True), (16, True)):
+        ws = None
+        if shared:
+            plan = pa.decode_plan(len(order), HKV * G, HKV, D, BS, mb, pa.DTYPE_BF16, psize, 0, shared_prefix=True)
+            ws = torch.zeros(plan["workspace_bytes"], dtype=torch.uint8, device=cuda)
         out = pa.paged_attention_decode(np_to_torch(q, "bf16").to(cuda), k_cache, v_cache,
                                         torch.from_numpy(tables).to(cuda), torch.from_numpy(lens).to(cuda), scale,
-                                        out_dtype=torch.float32, partition_size=psize)
+                                        out_dtype=torch.float32, partition_size=psize, shared_prefix=shared,
+                                        workspace=ws)
         torch.cuda.synchronize()
+        if shared:
+            # the sharing words are the workspace's last num_seqs int32 values (256-byte aligned)
+            tail = (len(order) * 4 + 255) // 256 * 256
+            end = plan["workspace_bytes"] - tail + len(order) * 4
+            words = ws[end - len(order) * 4:end].cpu().view(torch.int32).numpy()
+            want = expected_words(tables, lens, BS, G, nb, mb)
+            assert words.tolist() == want.tolist() and (want != 0).all(), (words, want)
         out = out.cpu().numpy()
         for i, s in enumerate(order):
             toks = seqs[s]
@@ -94,5 +109,5 @@ def test_manager_tables_drive_store_copy_and_decode(cuda):
             kd = oracle.widen(np.stack(ks), "bf16")
             vd = oracle.widen(np.stack(vs), "bf16")
             ref = oracle.decode_sequence(oracle.widen(q[i], "bf16"), kd, vd, scale)
-            assert np.abs(out[i] - ref).max() <= 2e-3, (psize, s)
+            assert np.abs(out[i] - ref).max() <= 2e-3, (psize, shared, s)
     m.close()
