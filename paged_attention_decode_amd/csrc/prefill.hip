@@ -54,6 +54,20 @@ constexpr int prefill_col_tiles(int dtype, int head_dim) {
                        : (head_dim <= 64 ? PA_PREFILL_NC64 : (head_dim <= 128 ? PA_PREFILL_NC128 : 1));
 }
 
+// p minus the fp16 value in the low (high) half of h, in one mixed-precision fma: the product
+// with -1 is exact and the sum is rounded once, so the result is the same as converting the
+// half to fp32 and subtracting, in one instruction instead of two.
+__device__ __forceinline__ float sub_f16_lo(float p, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(p));
+  return r;
+}
+__device__ __forceinline__ float sub_f16_hi(float p, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(p));
+  return r;
+}
+
 template <int DT, int D>
 struct PrefillCfg {
   using C = Cfg<DT, D>;
@@ -359,7 +373,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
 #pragma unroll
           for (int i2 = 0; i2 < 4; ++i2) {
             const auto hv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2], p[2 * i2 + 1]);
-            const auto lv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2] - (float)hv[0], p[2 * i2 + 1] - (float)hv[1]);
+            const uint32_t hb = __builtin_bit_cast(uint32_t, hv);
+            const auto lv = __builtin_amdgcn_cvt_pkrtz(sub_f16_lo(p[2 * i2], hb), sub_f16_hi(p[2 * i2 + 1], hb));
             ph[i2] = __builtin_bit_cast(uint32_t, hv);
             pl[i2] = __builtin_bit_cast(uint32_t, lv);
           }
@@ -739,7 +754,8 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
 #pragma unroll
           for (int i2 = 0; i2 < 4; ++i2) {
             const auto hv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2], p[2 * i2 + 1]);
-            const auto lv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2] - (float)hv[0], p[2 * i2 + 1] - (float)hv[1]);
+            const uint32_t hb = __builtin_bit_cast(uint32_t, hv);
+            const auto lv = __builtin_amdgcn_cvt_pkrtz(sub_f16_lo(p[2 * i2], hb), sub_f16_hi(p[2 * i2 + 1], hb));
             ph[i2] = __builtin_bit_cast(uint32_t, hv);
             pl[i2] = __builtin_bit_cast(uint32_t, lv);
           }
