@@ -21,7 +21,6 @@ them and ``k_cache_shape`` / ``v_cache_shape`` give the shapes:
 from __future__ import annotations
 
 import ctypes
-import os
 from pathlib import Path
 from typing import Optional, Tuple
 
@@ -32,8 +31,8 @@ __all__ = [
     "decode_step", "paged_prefill", "DEFAULT_CACHED_PREFIX_TOKENS",
 ]
 
-# PAGEDATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
-_LIB_PATH = Path(os.environ.get("PAGEDATTN_LIBRARY") or Path(__file__).resolve().with_name("libpagedattn.so"))
+# Always the in-tree build next to this file: the binding loads no other library.
+_LIB_PATH = Path(__file__).resolve().with_name("libpagedattn.so")
 _lib = None
 
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2

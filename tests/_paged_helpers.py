@@ -42,9 +42,13 @@ def physical_to_logical_v(v_phys: np.ndarray, nb, hkv, bs, d) -> np.ndarray:
 
 
 def widen_np(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 values of storage-form data through torch's own conversions (bf16 patterns are
+    uint16), independent of the oracle's widening."""
+    import torch
+    a = np.ascontiguousarray(a)
     if dtype == "bf16":
-        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return a.astype(np.float64)
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    return torch.from_numpy(a).to(torch.float64).numpy()
 
 
 class PagedCase:

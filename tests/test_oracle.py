@@ -52,6 +52,50 @@ def test_layout_golden_positions():
     np.testing.assert_array_equal(v2[fx["v_flat_positions"]], -row.ravel())
 
 
+# ---------------------------------------------------------------- widening of storage types
+
+def _ieee_half_value(bits: int, exp_bits: int, man_bits: int) -> float:
+    """Value of a 16-bit IEEE-style pattern from the format's definition (sign, biased exponent,
+    fraction; exponent 0 = subnormal, all ones = inf/NaN), independent of any conversion routine."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e = (bits >> man_bits) & ((1 << exp_bits) - 1)
+    f = bits & ((1 << man_bits) - 1)
+    bias = (1 << (exp_bits - 1)) - 1
+    if e == (1 << exp_bits) - 1:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, 1 - bias - man_bits)
+    return sign * math.ldexp((1 << man_bits) + f, e - bias - man_bits)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_widen_matches_torch_and_format_definition_on_every_bit_pattern(dtype):
+    """oracle.widen of all 65536 16-bit patterns equals torch's own conversion to float64 and the
+    value the format defines (bf16: 8 exponent / 7 fraction bits, fp16: 5 / 10), NaN as NaN."""
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):  # NaN patterns widen to NaN
+        got = oracle.widen(bits if dtype == "bf16" else bits.view(np.float16), dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    ref_torch = torch.from_numpy(bits.view(np.int16)).view(tdt).to(torch.float64).numpy()
+    eb, mb = (8, 7) if dtype == "bf16" else (5, 10)
+    ref_def = np.array([_ieee_half_value(int(b), eb, mb) for b in bits])
+    for ref in (ref_torch, ref_def):
+        nan = np.isnan(ref)
+        np.testing.assert_array_equal(np.isnan(got), nan)
+        np.testing.assert_array_equal(got[~nan], ref[~nan])
+        # signed zeros keep their sign
+        np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert got.dtype == np.float64
+
+
+def test_widen_fp32_is_exact():
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal(1000).astype(np.float32)
+    a[:4] = [0.0, -0.0, np.float32(2.0 ** -149), np.float32(3.4e38)]
+    np.testing.assert_array_equal(oracle.widen(a, "fp32"), np.array([float(v) for v in a.tolist()]))
+
+
 # ---------------------------------------------------------------- brute force vs library routine
 
 @settings(max_examples=40, deadline=None, suppress_health_check=[HealthCheck.too_slow])

@@ -92,6 +92,7 @@ def test_generation_is_deterministic_and_seeded():
 
 def test_values_are_rounded_normal_draws():
     x = make_inputs(get_config("qwen3_0p6b_bf16"))
-    v = (x.k_cache[:200000].astype(np.uint32) << 16).view(np.float32)
+    import torch
+    v = torch.from_numpy(x.k_cache[:200000].view(np.int16)).view(torch.bfloat16).float().numpy()
     assert abs(v.mean()) < 0.02 and abs(v.std() - 1) < 0.02
     assert x.k_cache.size == x.num_blocks * 8 * 256 * 128
