@@ -86,6 +86,58 @@ def test_full_config_store_bit_exact_and_decode_parity(cuda, name):
     torch.cuda.empty_cache()
 
 
+def test_long_context_in_512_token_partitions_full_size(cuda):
+    """The 16 x 32768-token workload as specified: fixed 512-token partitions, each segment's 64
+    pieces merged by the log-sum-exp reduce kernel. Store bit-exact over both whole caches;
+    decode of sampled sequences (first, last and two seeded others) against the oracle."""
+    import torch
+    import paged_attention_decode_amd as pa
+    _say("[gpu] long_ctx_bf16 at partition_size=512: generating")
+    x = _inputs("long_ctx_bf16")
+    c = x.cfg
+    plan = pa.decode_plan(c.batch, c.num_heads, c.num_kv_heads, c.head_dim, c.block_size, c.max_blocks_per_seq,
+                          pa.DTYPE_BF16, partition_size=512)
+    assert plan["range_tokens"] == 512 and plan["uses_reduce"]
+    # every context is 64 whole partitions, so every segment is cut into 64 merged pieces
+    assert (x.context_lens == 32768).all()
+    seqs = sorted({0, c.batch - 1, *np.random.default_rng(4).choice(np.arange(1, c.batch - 1), 2, replace=False)})
+    dev = to_device(x, cuda)
+    _say(f"[gpu] long_ctx_bf16 at partition_size=512: store + decode, checking sequences {seqs}")
+    out = _run_step(dev, x, partition_size=512).cpu().numpy()
+    k2, v2, ref = oracle_after_store(x, seqs=seqs)
+    assert torch_to_np(dev["k_cache"], c.dtype).reshape(-1).tobytes() == k2.reshape(-1).tobytes()
+    assert torch_to_np(dev["v_cache"], c.dtype).reshape(-1).tobytes() == v2.reshape(-1).tobytes()
+    assert np.isfinite(out).all()
+    err = np.abs(out[seqs] - ref[seqs]).max()
+    _say(f"[gpu] long_ctx_bf16 at 512: max-abs error {err:.3e}")
+    assert err <= TOL[c.dtype]
+    # bf16 output: one extra round-to-nearest-even at most
+    out_t = _run_step(dev, x, partition_size=512, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert (np.abs(out_t[seqs] - ref[seqs]) <= TOL[c.dtype] + half_ulp(ref[seqs], c.dtype)).all()
+    del dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b_bf16", "llama32_1b_fp16"])
+def test_torch_gather_mask_comparator_matches_oracle(cuda, name):
+    """The benchmark's PyTorch comparator (batched gather through the block tables, masked
+    softmax, weighted sum) computes the oracle's result on the workload's own inputs."""
+    import torch
+    from bench import torch_gather_mask_decode
+    _say(f"[gpu] comparator {name}")
+    x = _inputs(name)
+    dev = to_device(x, cuda)
+    ref = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, x.scale, geometry(x))
+    got = torch_gather_mask_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                   dev["context_lens"], x.scale, int(x.context_lens.max()))
+    got = got.float().cpu().numpy()
+    err = np.abs(got - ref).max()
+    _say(f"[gpu] comparator {name}: max-abs error {err:.3e}")
+    assert err <= TOL[x.cfg.dtype]
+    del dev
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("psize", [-3, -2, -1, 0, 16, 48, 512])
 @pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"])
 def test_launch_modes_agree_with_oracle(cuda, name, psize):
