@@ -239,6 +239,39 @@ int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void*
                                  const pa_decode_opts* opts, void* stream);
 
 /*
+ * pa_paged_attention_decode_noalloc - pa_paged_attention_decode_ex without any
+ * device-memory allocation.
+ *
+ * For callers that cannot allocate: code being recorded into a HIP graph,
+ * serving loops that must not call the allocator, harnesses that forbid it.
+ * Arguments, result and errors as for pa_paged_attention_decode_ex (the same
+ * kernels run), except:
+ *  - The split modes' workspace is a fixed array of PA_NOALLOC_SCRATCH_BYTES
+ *    of device memory inside the library, one per device, held from the first
+ *    call on that device until the process ends. That first call looks up the
+ *    array's device address (set-up, outside any graph capture); no call
+ *    allocates, frees or calls an allocating routine.
+ *  - opts->workspace must be NULL (PA_ERR_WORKSPACE otherwise).
+ *  - A call whose plan needs more workspace than PA_NOALLOC_SCRATCH_BYTES
+ *    (pa_decode_plan_ex reports the figure) returns PA_ERR_WORKSPACE and
+ *    enqueues nothing. One pass and workgroup split need none.
+ *  - Every call on a device uses that device's one array, which keeps the last
+ *    call's contents (nothing in it needs to start at zero). Calls that may
+ *    overlap on one device (other streams, other host threads) race on it: the
+ *    caller must serialise them.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int pa_paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      float scale, void* out,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int64_t q_seq_stride,
+                                      int32_t dtype, int32_t out_dtype,
+                                      const pa_decode_opts* opts, void* stream);
+
+/*
  * pa_decode_step - the decode step's scatter and attention in one launch.
  *
  * Same result as pa_store_kvcache of each sequence's new token followed by

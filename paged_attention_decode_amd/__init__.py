@@ -28,7 +28,8 @@ __all__ = [
     "PagedAttnError", "store_kvcache", "paged_attention_decode", "allocate_kv_cache",
     "k_cache_shape", "v_cache_shape", "decode_plan", "workspace_bytes", "version", "shutdown",
     "library_path", "load_library", "DTYPE_F32", "DTYPE_F16", "DTYPE_BF16", "BlockManager", "copy_blocks",
-    "decode_step", "paged_prefill", "DEFAULT_CACHED_PREFIX_TOKENS",
+    "decode_step", "paged_prefill", "DEFAULT_CACHED_PREFIX_TOKENS", "paged_attention_decode_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 # Always the in-tree build next to this file: the binding loads no other library.
@@ -38,6 +39,8 @@ _lib = None
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 # PA_DEFAULT_CACHED_PREFIX_TOKENS: what cached_prefix_tokens = 0 selects.
 DEFAULT_CACHED_PREFIX_TOKENS = 1024
+# PA_NOALLOC_SCRATCH_BYTES: the fixed workspace of pa_paged_attention_decode_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_UNSUPPORTED",
            5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY"}
 
@@ -81,6 +84,8 @@ def load_library():
     lib.pa_paged_attention_decode.restype = c_int
     lib.pa_paged_attention_decode_ex.argtypes = dec + [ctypes.POINTER(DecodeOpts), c_p]
     lib.pa_paged_attention_decode_ex.restype = c_int
+    lib.pa_paged_attention_decode_noalloc.argtypes = dec + [ctypes.POINTER(DecodeOpts), c_p]
+    lib.pa_paged_attention_decode_noalloc.restype = c_int
     lib.pa_decode_step.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_f, c_p, c_int, c_int, c_int,
                                    c_int, c_int, c_int, c_i64, c_i64, c_int, c_int, ctypes.POINTER(DecodeOpts), c_p]
     lib.pa_decode_step.restype = c_int
@@ -288,6 +293,48 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         opts.event_begin = events[0].cuda_event
         opts.event_end = events[1].cuda_event
     _check(lib.pa_paged_attention_decode_ex(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+        float(scale), out.data_ptr(), bsz, hq, hkv, d, bs, bts[1], nb, qst[0],
+        _dtype_code(q.dtype), _dtype_code(out.dtype), ctypes.byref(opts), _stream_of(q)))
+    return out
+
+
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
+                                   partition_size: int = 0, cached_prefix_tokens: int = 0, events=None,
+                                   shared_prefix: bool = False):
+    """pa_paged_attention_decode_noalloc: paged_attention_decode into a caller-given ``out`` with
+    the library's fixed scratch as workspace; the call allocates no device memory (raises
+    PagedAttnError PA_ERR_WORKSPACE when the plan needs more than NOALLOC_SCRATCH_BYTES)."""
+    import torch
+    lib = _lib or load_library()
+    _require_cuda(q, k_cache, v_cache, block_tables, context_lens, out)
+    nb, hkv, d, bs = _cache_geometry(k_cache, v_cache)
+    qs, qst = q.shape, q.stride()
+    if len(qs) != 3 or qs[2] != d or qst[1:] != (d, 1):
+        raise ValueError(f"q must be [B, Hq, {d}] with contiguous head rows")
+    bsz, hq = qs[0], qs[1]
+    if q.dtype != k_cache.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    bts = block_tables.shape
+    if len(bts) != 2 or bts[0] != bsz or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous [B, max_blocks] tensor")
+    if context_lens.shape != (bsz,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] tensor")
+    if out.shape != (bsz, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor")
+    opts = DecodeOpts()
+    opts.partition_size = int(partition_size)
+    opts.cached_prefix_tokens = int(cached_prefix_tokens)
+    opts.shared_prefix = 1 if shared_prefix else 0
+    if events is not None:
+        for ev in events:
+            if not ev.cuda_event:
+                ev.record()
+        opts.event_begin = events[0].cuda_event
+        opts.event_end = events[1].cuda_event
+    _check(lib.pa_paged_attention_decode_noalloc(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
         float(scale), out.data_ptr(), bsz, hq, hkv, d, bs, bts[1], nb, qst[0],
         _dtype_code(q.dtype), _dtype_code(out.dtype), ctypes.byref(opts), _stream_of(q)))

@@ -52,6 +52,8 @@ struct DeviceState {
   int num_cus = 0;
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  // Device address of this device's copy of `scratch` (below), once looked up.
+  void* scratch_ptr = nullptr;
 };
 
 // Fixed storage, so a DeviceState pointer stays valid while other threads
@@ -213,6 +215,25 @@ int device_state(DeviceState** out) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workspace of pa_paged_attention_decode_noalloc: fixed device memory, one copy per device,
+// held until the process ends. In host code `scratch` names a host-side stand-in, not device
+// memory: host code uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+// Looks up (once per device, with that device current) the device address of `scratch`.
+int scratch_address(DeviceState* st, void** out) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!st->scratch_ptr) {
+    void* ptr = nullptr;
+    hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(err));
+    st->scratch_ptr = ptr;
+  }
+  *out = st->scratch_ptr;
+  return PA_OK;
+}
 
 }  // namespace
 
@@ -410,8 +431,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                 int64_t num_blocks, int64_t q_seq_stride, int32_t dtype, int32_t out_dtype,
                 const pa_decode_opts* opts, void* stream, const void* k_new, const void* v_new,
-                int64_t k_new_stride, int64_t v_new_stride) {
+                int64_t k_new_stride, int64_t v_new_stride, bool noalloc = false) {
   const int32_t psize = opts ? opts->partition_size : 0;
+  if (noalloc && opts && opts->workspace)
+    return fail(PA_ERR_WORKSPACE, "the no-allocation entry point uses its fixed scratch; opts->workspace must be NULL");
   int rc = check_decode_sizes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, dtype,
                               psize);
   if (rc != PA_OK) return rc;
@@ -438,7 +461,17 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
 
   char* ws = nullptr;
   if (p.ws_bytes > 0) {
-    if (opts && opts->workspace) {
+    if (noalloc) {
+      if (p.ws_bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+        return fail(PA_ERR_WORKSPACE,
+                    "this call's plan needs %zu bytes of workspace, more than the %zu-byte fixed scratch of "
+                    "pa_paged_attention_decode_noalloc",
+                    p.ws_bytes, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+      void* sp = nullptr;
+      rc = scratch_address(st, &sp);
+      if (rc != PA_OK) return rc;
+      ws = reinterpret_cast<char*>(sp);
+    } else if (opts && opts->workspace) {
       if (opts->workspace_bytes < p.ws_bytes)
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", opts->workspace_bytes, p.ws_bytes);
       if ((reinterpret_cast<uintptr_t>(opts->workspace) & 255u) != 0)
@@ -541,6 +574,17 @@ int pa_paged_attention_decode_ex(const void* q, const void* k_cache, const void*
   return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_heads, num_kv_heads,
                      head_dim, block_size, max_blocks_per_seq, num_blocks, q_seq_stride, dtype, out_dtype, opts,
                      stream, nullptr, nullptr, 0, 0);
+}
+
+int pa_paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                      void* out, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int64_t q_seq_stride, int32_t dtype, int32_t out_dtype,
+                                      const pa_decode_opts* opts, void* stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_heads, num_kv_heads,
+                     head_dim, block_size, max_blocks_per_seq, num_blocks, q_seq_stride, dtype, out_dtype, opts,
+                     stream, nullptr, nullptr, 0, 0, /*noalloc=*/true);
 }
 
 int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride, int64_t v_new_stride,

@@ -39,6 +39,8 @@ def test_binding_constants_match_the_header():
     text = HEADER.read_text()
     m = re.search(r"#define\s+PA_DEFAULT_CACHED_PREFIX_TOKENS\s+(\d+)", text)
     assert m and int(m.group(1)) == pa.DEFAULT_CACHED_PREFIX_TOKENS
+    m = re.search(r"#define\s+PA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_SCRATCH_BYTES
     for name, code in (("PA_DTYPE_F32", pa.DTYPE_F32), ("PA_DTYPE_F16", pa.DTYPE_F16), ("PA_DTYPE_BF16", pa.DTYPE_BF16)):
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
 
