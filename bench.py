@@ -6,16 +6,26 @@ token per sequence, then paged_attention_decode (attention kernel plus, when
 contexts are split, the merge kernel). Inputs are seeded synthetic data of the
 workload's shape, resident in HBM before timing starts.
 
+Each workload is timed twice over K steps: a warm loop (steps back to back,
+wall clock around all K) and a cold loop (each step after a 1 GiB read that
+evicts the K/V from the L2s and the last-level cache, outside the events).
+
 Prints ONE JSON line:
-  value        KV GB/s: logical K+V bytes one decode must read (sum over
-               sequences of L * Hkv * D * 2 bytes * 2) / wall time per step
+  value        KV GB/s of the warm loop: logical K+V bytes one decode must read
+               (sum over sequences of L * Hkv * D * e * 2) / wall time per step
   tokens_per_s sequences advanced per second (B / time per step)
-  roofline     the attention kernel alone: the same KV bytes / its mean
-               duration from HIP events recorded on its stream, against
-               MI355X's 8 TB/s HBM peak; traffic from committed rocprofv3
-               counter summaries when they match the current kernel source
+  roofline     the attention kernel alone, cold: the same KV bytes / the mean
+               duration of its cold-loop launches (HIP events on its stream),
+               against MI355X's 8 TB/s HBM peak and against the measured
+               streaming-read ceiling; the warm figure beside it; traffic from
+               committed rocprofv3 counter summaries when they match the
+               current kernel source
+  cold_step, split_cold_median_us   cold step time and its store / attention /
+               merge-and-gaps split
+  stream_read_ceiling  best rate of a plain streaming-read kernel on the box
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample
                of the same workload (a reported baseline, not the target)
+  workloads    (default run) the same record for each other workload
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload NAME] [--prefill]
 """
@@ -36,6 +46,12 @@ sys.path.insert(0, str(ROOT))
 METRIC = "paged-attn decode KV HBM GB/s (% of MI355X peak) and decode tokens/s"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "skewed_prefix_bf16"
+# The default run also measures these workloads, each in a record of its own.
+RECORD_WORKLOADS = ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16", "long_ctx_bf16"]
+# Launch mode a workload is specified with (others: 0, the library's automatic choice).
+WORKLOAD_PARTITION = {"long_ctx_bf16": 512}
+# Workloads whose CPU baseline is also taken with one BLAS thread.
+ONE_THREAD_BASELINE = {"tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"}
 KERNEL_SOURCE = ROOT / "paged_attention_decode_amd" / "csrc" / "decode.hip"
 PROFILES = ROOT / "profiles"
 COPY_BYTES = 256 << 20
@@ -46,9 +62,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--partition-size", type=int, default=0,
-                    help="0 automatic, -1 one pass, -2 balanced split, >0 fixed ranges of that many tokens")
+    ap.add_argument("--workload", default=None,
+                    help=f"time this workload only (default: {DEFAULT_WORKLOAD} as the headline, plus a record "
+                         "for each other workload)")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="0 automatic, -1 one pass, -2 balanced split, -3 workgroup split, >0 fixed ranges of "
+                         "that many tokens (default: the workload's own, 512 for the long-context one, else 0)")
     ap.add_argument("--cached-prefix-tokens", type=int, default=0,
                     help="leading tokens per context read with cached loads (0 library default, -1 none)")
     ap.add_argument("--shared-prefix", action="store_true",
@@ -63,11 +82,13 @@ def parse():
                     help="time replays of one step captured into a HIP graph instead of eager launches")
     ap.add_argument("--comparators", action="store_true",
                     help="also time a PyTorch gather-and-mask decode on the same inputs (benchmark only)")
-    ap.add_argument("--cold-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush each")
+    ap.add_argument("--no-records", action="store_true",
+                    help="default run without the records of the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-timings", action="store_true",
                     help="skip the per-call and per-mode timings (profiled runs: only the timed steps launch)")
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0, help="target seconds of oracle work")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0,
+                    help="target seconds of oracle work for the headline workload (3 s for each record)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/decode_<workload>_traffic.txt from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, then WRITE_SIZE) of this script, then exit")
@@ -81,7 +102,9 @@ def parse():
                     help="write profiles/<kernel>_<workload>_sq_counters.txt from rocprofv3 --pmc runs of SQ_ "
                          "counters (the attention kernel, or the prefill kernel with --prefill), then exit")
     ap.add_argument("--sq-commands", nargs="*", default=[], help="the profiling commands, recorded in the summary")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.workload_given = args.workload is not None
+    return args
 
 
 class TimingEvent:
@@ -127,8 +150,9 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
-            TimingEvent._hip.hipEventDestroy(self.cuda_event)
+        hip = getattr(type(self), "_hip", None)  # None once the interpreter is tearing down
+        if hip is not None and getattr(self, "cuda_event", None):
+            hip.hipEventDestroy(self.cuda_event)
 
 
 def kernel_source_sha(kernel: str = "decode") -> str:
@@ -337,34 +361,61 @@ def describe(cfg) -> dict:
     return d
 
 
-def cpu_baseline(x, gpu_out, budget_s: float) -> dict:
-    """Time the float64 oracle on a bounded sample of the batch and compare it with the GPU output."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, gpu_out, budget_s: float, one_thread_budget_s: float = 0.0) -> dict:
+    """Time the float64 oracle on a bounded sample of the batch and compare it with the GPU output.
+
+    Sequences are taken one at a time in a seeded order until the budget is spent or the batch
+    is done. With one_thread_budget_s > 0 the same is repeated with the BLAS pool limited to one
+    thread."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     c = x.cfg
     geo = oracle.CacheGeometry(x.num_blocks, c.num_kv_heads, c.head_dim, c.block_size, c.dtype)
     k2, v2 = oracle.store_kvcache(x.k_new, x.v_new, x.slot_mapping, x.k_cache, x.v_cache, geo)
-    # sequences in a seeded order, in chunks, until the time budget is spent or the batch is done
-    order = np.random.default_rng(12345).permutation(c.batch).tolist()
-    seqs, tokens, dt = [], 0, 0.0
     ref = np.zeros((c.batch, c.num_heads, c.head_dim))
-    while order and dt < budget_s:
-        chunk, order = order[:8], order[8:]
-        t = time.perf_counter()
-        part = oracle.decode(x.q, k2, v2, x.block_tables, x.context_lens, x.scale, geo, seqs=chunk)
-        dt += time.perf_counter() - t
-        ref[chunk] = part[chunk]
-        seqs += chunk
-        tokens += int(x.context_lens[chunk].sum())
+
+    def timed(budget):
+        order = np.random.default_rng(12345).permutation(c.batch).tolist()
+        seqs, tokens, dt = [], 0, 0.0
+        while order and dt < budget:
+            s = order.pop(0)
+            t = time.perf_counter()
+            part = oracle.decode(x.q, k2, v2, x.block_tables, x.context_lens, x.scale, geo, seqs=[s])
+            dt += time.perf_counter() - t
+            ref[s] = part[s]
+            seqs.append(s)
+            tokens += int(x.context_lens[s])
+        return seqs, tokens, dt
+
+    seqs, tokens, dt = timed(budget_s)
     kv = tokens * c.num_kv_heads * c.head_dim * c.elem_bytes * 2
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     err = float(np.abs(gpu_out[seqs] - ref[seqs]).max())
-    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(seqs)} of {c.batch} sequences ({tokens} context tokens) after the step's scatter, float64 numpy",
-            "seconds": dt, "tokens_per_s": len(seqs) / dt, "host_cpus": len(os.sched_getaffinity(0)),
-            "parity_max_abs_err_vs_gpu": err}
+    res = {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{len(seqs)} of {c.batch} sequences ({tokens} context tokens) after the step's scatter, "
+                     f"float64 numpy, one sequence per call",
+           "seconds": dt, "tokens_per_s": len(seqs) / dt, "host_cpus": len(os.sched_getaffinity(0)),
+           "cpu_model": cpu_model(), "parity_max_abs_err_vs_gpu": err}
+    if one_thread_budget_s > 0:
+        with threadpool_limits(limits=1):
+            seqs1, tokens1, dt1 = timed(one_thread_budget_s)
+        kv1 = tokens1 * c.num_kv_heads * c.head_dim * c.elem_bytes * 2
+        res["one_thread"] = {"value": kv1 / dt1 / 1e9, "unit": "GB/s", "cores": 1, "seconds": dt1,
+                             "sample": f"{len(seqs1)} of {c.batch} sequences ({tokens1} context tokens)",
+                             "tokens_per_s": len(seqs1) / dt1}
+    return res
 
 
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
@@ -377,11 +428,8 @@ def _pcts(ms):
             "p90_us": round(float(np.percentile(a, 90)), 2)}
 
 
-def extra_timings(calls: dict, reps: int, stream_bytes: int, dev) -> dict:
-    """Per-call event timings (p10 / median / p90) of each callable, measured back to back.
-
-    Also times torch's sum over `stream_bytes` of fp32 as a plain streaming-read reference rate.
-    """
+def extra_timings(calls: dict, reps: int) -> dict:
+    """Per-call event timings (p10 / median / p90) of each callable, measured back to back."""
     import torch
     out = {}
     for name, fn in calls.items():
@@ -394,21 +442,91 @@ def extra_timings(calls: dict, reps: int, stream_bytes: int, dev) -> dict:
             e.record()
         torch.cuda.synchronize()
         out[name] = _pcts([b.elapsed_time(e) for b, e in evs])
-    buf = torch.ones(stream_bytes // 4, dtype=torch.float32, device=dev)
-    buf.sum()
-    torch.cuda.synchronize()
-    evs = [(TimingEvent(), TimingEvent()) for _ in range(5)]
-    for b, e in evs:
-        b.record()
-        buf.sum()
-        e.record()
-    torch.cuda.synchronize()
-    best = min(b.elapsed_time(e) for b, e in evs)
-    out["stream_read_reference"] = {"gbs": round(stream_bytes / (best * 1e-3) / 1e9, 1),
-                                    "what": f"torch.sum over {stream_bytes >> 30} GiB fp32, best of 5"}
-    del buf
-    torch.cuda.empty_cache()
     return out
+
+
+class StreamRead:
+    """The streaming-read kernel of libpa_stream_read.so (measurement only) over one buffer."""
+
+    BYTES = (1 << 31) - (1 << 14)
+
+    def __init__(self, dev):
+        import ctypes
+        import torch
+        lib_path = ROOT / "paged_attention_decode_amd" / "libpa_stream_read.so"
+        if not lib_path.exists():
+            raise RuntimeError(f"{lib_path} is not built: run `python -m paged_attention_decode_amd.build`")
+        self.lib = ctypes.CDLL(str(lib_path))
+        self.lib.pa_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.pa_bench_stream_read.restype = ctypes.c_int
+        self.cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        self.buf = torch.empty(self.BYTES, dtype=torch.uint8, device=dev)
+        self.sink = torch.empty(self.cus * 16 * 4 * 64, dtype=torch.int32, device=dev)
+        self.dev = dev
+        self.ceiling_gbs = None  # best rate of ceiling(), once measured
+        self.best = None
+
+    def read(self, nbytes, policy=0, unroll=8, groups_per_cu=4):
+        import torch
+        grid = self.cus * groups_per_cu
+        assert grid * 4 * 64 <= self.sink.numel() and nbytes <= self.BYTES
+        rc = self.lib.pa_bench_stream_read(self.buf.data_ptr(), nbytes, policy, unroll, grid, self.sink.data_ptr(),
+                                           torch.cuda.current_stream(self.dev).cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"pa_bench_stream_read failed ({rc})")
+
+    def flush(self):
+        """Read 1 GiB with the default policy: afterwards the L2s and the last-level cache hold none
+        of the benchmark's K/V (reads leave no dirty lines to write back during the next step)."""
+        self.read(1 << 30, 0, 8, 4)
+
+    def same_bytes(self, nbytes: int, reps: int = 10) -> dict:
+        """Cold read of as many bytes as a workload's K/V (rounded down to 16 KiB), with the best
+        setting of ceiling(): the practical ceiling at that size, launch ramp and tail included."""
+        import torch
+        n = max(1 << 14, min(self.BYTES, nbytes) // (1 << 14) * (1 << 14))
+        b = self.best or {"policy": "nt", "unroll": 8, "groups_per_cu": 4}
+        pol = 1 if b["policy"] == "nt" else 0
+        self.read(n, pol, b["unroll"], b["groups_per_cu"])
+        ms = []
+        for _ in range(reps):
+            self.flush()
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record()
+            self.read(n, pol, b["unroll"], b["groups_per_cu"])
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        med = sorted(ms)[len(ms) // 2]
+        return {"bytes": n, "median_us": round(med * 1e3, 2), "gbs": round(n / (med * 1e-3) / 1e9, 1),
+                "setting": b, "what": "cold (after a 1 GiB read), median of " + str(reps)}
+
+    def ceiling(self, reps: int = 5) -> dict:
+        """Best rate over a small sweep of loads in flight and occupancy, per cache policy."""
+        import torch
+        rows = []
+        for policy in (0, 1):
+            for unroll in (8, 16):
+                for gpc in (2, 4, 8):
+                    self.read(self.BYTES, policy, unroll, gpc)
+                    torch.cuda.synchronize()
+                    evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+                    for b, e in evs:
+                        b.record()
+                        self.read(self.BYTES, policy, unroll, gpc)
+                        e.record()
+                    torch.cuda.synchronize()
+                    best = min(b.elapsed_time(e) for b, e in evs)
+                    rows.append({"policy": "nt" if policy else "default", "unroll": unroll, "groups_per_cu": gpc,
+                                 "gbs": round(self.BYTES / (best * 1e-3) / 1e9, 1)})
+        top = max(rows, key=lambda r: r["gbs"])
+        self.best = top
+        by_pol = {p: max(r["gbs"] for r in rows if r["policy"] == p) for p in ("default", "nt")}
+        return {"gbs": top["gbs"], "best": top, "best_default_policy_gbs": by_pol["default"],
+                "best_nt_policy_gbs": by_pol["nt"], "bytes": self.BYTES,
+                "what": "pa_bench_stream_read: 16-byte buffer loads, 1 KiB per wavefront load instruction, "
+                        f"one pass over {self.BYTES} bytes, best of {reps} per setting", "sweep": rows}
 
 
 def prefill_useful_flops(head_dim: int, num_heads: int, new_tokens, context_lens) -> float:
@@ -477,90 +595,88 @@ def prefill_bench(args) -> None:
                      "kernel_mean_ms": round(ms, 5)}}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.summarize_pmc:
-        print(summarize_pmc(args.workload, args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands))
-        return
-    if args.summarize_sq:
-        print(summarize_sq(args.workload, args.summarize_sq, args.sq_commands, "prefill" if args.prefill else "decode"))
-        return
-    if args.summarize_trace:
-        print(summarize_trace(args.workload, args.summarize_trace, args.trace_command,
-                              "prefill" if args.prefill else "decode"))
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the library "
-              "has no cross-GPU step; each GPU would run its own shard of sequences or kv heads", file=sys.stderr)
-        sys.exit(2)
+def _upload(a, dtype, dev):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+
+def _stats_us(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"mean_us": round(float(a.mean()), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "median_us": round(float(np.median(a)), 2), "p90_us": round(float(np.percentile(a, 90)), 2)}
+
+
+def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> dict:
+    """Time the decode step of one workload: a warm loop of K steps (wall clock and per-launch events
+    of the attention kernel), then K cold steps, each after a 1 GiB read (outside the events), with
+    events around the store, the attention kernel and the whole step. The roofline is taken on the
+    cold attention-kernel launches."""
     import numpy as np
     import torch
 
     import paged_attention_decode_amd as pa
     from workloads import get_config, make_inputs
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    pa.load_library()
-    if args.prefill:
-        prefill_bench(args)
-        return
-    dev = torch.device("cuda:0")
-    cfg = get_config(args.workload)
-    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    cfg = get_config(name)
+    psize = args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(name, 0)
+    print(f"[bench] {name}: generating", file=sys.stderr, flush=True)
     x = make_inputs(cfg)
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
-
-    def up(a):
-        if cfg.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    k_cache = up(x.k_cache).view(pa.k_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, tdt))
-    v_cache = up(x.v_cache).view(pa.v_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size))
-    q, k_new, v_new = up(x.q), up(x.k_new), up(x.v_new)
+    k_cache = _upload(x.k_cache, cfg.dtype, dev).view(
+        pa.k_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, tdt))
+    v_cache = _upload(x.v_cache, cfg.dtype, dev).view(
+        pa.v_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size))
+    q, k_new, v_new = (_upload(a, cfg.dtype, dev) for a in (x.q, x.k_new, x.v_new))
     block_tables = torch.from_numpy(x.block_tables).to(dev)
     context_lens = torch.from_numpy(x.context_lens).to(dev)
     slots = torch.from_numpy(x.slot_mapping).to(dev)
     out = torch.empty((cfg.batch, cfg.num_heads, cfg.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    def store():
+        pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache)
+
+    def decode(events=None, psz=psize, shared=args.shared_prefix):
+        pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
+                                  partition_size=psz, cached_prefix_tokens=args.cached_prefix_tokens,
+                                  events=events, shared_prefix=shared)
+
     def step(events=None):
         if args.fused_step:
             pa.decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, x.scale, out,
-                           partition_size=args.partition_size, cached_prefix_tokens=args.cached_prefix_tokens,
+                           partition_size=psize, cached_prefix_tokens=args.cached_prefix_tokens,
                            events=events, shared_prefix=args.shared_prefix)
             return
-        pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache)
-        pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
-                                  partition_size=args.partition_size,
-                                  cached_prefix_tokens=args.cached_prefix_tokens, events=events,
-                                  shared_prefix=args.shared_prefix)
+        store()
+        decode(events)
 
-    # A plain copy of known size (COPY_BYTES read + written): counter runs scale HBM bytes by it.
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
+    if headline:
+        # A plain copy of known size (COPY_BYTES read + written): counter runs scale HBM bytes by it.
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # The first call allocates the library's workspace; warm-up keeps that out of the timed region.
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
-
-    events = [(TimingEvent(), TimingEvent())
-              for _ in range(args.steps)]
-    for e in events:  # materialise the HIP events outside the timed region
-        e[0].record(stream)
-        e[1].record(stream)
+    K = args.steps
+    kev = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+    cev = [[TimingEvent() for _ in range(5)] for _ in range(K)]
+    for e in kev + [tuple(c) for c in cev]:  # materialise the HIP events outside the timed region
+        for ev in e:
+            ev.record(stream)
     torch.cuda.synchronize()
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    # Warm loop (the whole-job figure): K steps back to back, wall clock around them.
+    print(f"[bench] {name}: timing {K} steps", file=sys.stderr, flush=True)
     if args.graph:
         # One step captured into a HIP graph and replayed K times. Events recorded inside a
         # captured graph do not bracket the kernel, so the attention kernel is timed by an
@@ -571,54 +687,112 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for _ in range(K):
             graph.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        for i in range(args.steps):
-            step(events[i])
+        for i in range(K):
+            step(kev[i])
         torch.cuda.synchronize()
-        kernel_ms = [e[0].elapsed_time(e[1]) for e in events]
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(events[i])
+        for i in range(K):
+            step(kev[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kernel_ms = [e[0].elapsed_time(e[1]) for e in events]
+    warm_kernel_ms = [b.elapsed_time(e) for b, e in kev]
 
-    ms_per_step = wall * 1e3 / args.steps
+    # Cold loop: each step after a 1 GiB read, so no K/V is in the L2s or the last-level cache.
+    # Events: c0 step start, c1 after the store, (c2, c3) the attention kernel, c4 step end.
+    print(f"[bench] {name}: timing {K} cold steps", file=sys.stderr, flush=True)
+    for i in range(K):
+        sr.flush()
+        c = cev[i]
+        c[0].record(stream)
+        if args.fused_step:
+            step((c[2], c[3]))
+            c[1] = c[0]
+        else:
+            store()
+            c[1].record(stream)
+            decode((c[2], c[3]))
+        c[4].record(stream)
+    torch.cuda.synchronize()
+    cold_kernel_ms = [c[2].elapsed_time(c[3]) for c in cev]
+    cold_step_ms = [c[0].elapsed_time(c[4]) for c in cev]
+    cold_store_ms = [c[0].elapsed_time(c[1]) for c in cev]
+    cold_decode_ms = [c[1].elapsed_time(c[4]) for c in cev]
+    gpu_out = out.cpu().numpy()
+    same = sr.same_bytes(x.unique_kv_bytes if args.shared_prefix else x.kv_bytes) if sr.best else None
+
+    ms_per_step = wall * 1e3 / K
     kv_bytes = x.kv_bytes
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    mean_kernel_ms = sum(kernel_ms) / len(kernel_ms)
-    achieved = kv_bytes / (mean_kernel_ms * 1e-3) / 1e9
-    # The distinct K/V bytes of the batch (a block shared by several sequences counted once): the
-    # least any kernel must read. Logical bytes above it are re-reads that caches or the
-    # shared-prefix option serve.
-    achieved_unique = x.unique_kv_bytes / (mean_kernel_ms * 1e-3) / 1e9
     # With shared prefixes the kernel reads each shared block once: its algorithmic bytes are the
     # distinct ones, and the roofline is taken on those.
-    roof_bytes = "distinct K/V bytes (shared blocks once)" if args.shared_prefix else "logical K/V bytes"
-    roof_achieved = achieved_unique if args.shared_prefix else achieved
-
-    # Steps timed after overwriting 1 GiB, so last-level caches hold no KV (reported beside the main figure).
-    cold = []
-    if args.cold_steps > 0:
-        # reading (not writing) 1 GiB leaves no dirty lines to be written back during the step
-        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        for _ in range(args.cold_steps):
-            scratch.sum()
-            ev = (TimingEvent(), TimingEvent())
-            step(ev)
-            torch.cuda.synchronize()
-            cold.append(ev[0].elapsed_time(ev[1]))
-        del scratch
-
-    comparators = None
+    roof_bytes = x.unique_kv_bytes if args.shared_prefix else kv_bytes
+    cold_mean = float(np.mean(cold_kernel_ms))
+    warm_mean = float(np.mean(warm_kernel_ms))
+    achieved = roof_bytes / (cold_mean * 1e-3) / 1e9
+    warm_achieved = roof_bytes / (warm_mean * 1e-3) / 1e9
+    cold_step_median = float(np.median(cold_step_ms))
+    plan = pa.decode_plan(cfg.batch, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size,
+                          int(x.block_tables.shape[1]), {"fp32": 0, "fp16": 1, "bf16": 2}[cfg.dtype], psize, 0,
+                          shared_prefix=args.shared_prefix)
+    rec = {
+        "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
+                       partition_size=psize, plan_range_tokens=plan["range_tokens"],
+                       merge_kernel=plan["uses_reduce"], shared_prefix=bool(args.shared_prefix),
+                       cached_prefix_tokens=args.cached_prefix_tokens or pa.DEFAULT_CACHED_PREFIX_TOKENS,
+                       launch="hip graph replay" if args.graph else "eager",
+                       step="pa_decode_step (fused scatter + attention)" if args.fused_step
+                       else "pa_store_kvcache + pa_paged_attention_decode"),
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "ms_per_step": round(ms_per_step, 5),
+        "tokens_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
+        "cold_step": dict(_stats_us(cold_step_ms),
+                          kv_gbs=round(kv_bytes / (cold_step_median * 1e-3) / 1e9, 2),
+                          tokens_per_s=round(cfg.batch / (cold_step_median * 1e-3), 1),
+                          note="events around each cold step (store, attention, merge); the events' own "
+                               "recording adds a few us per step on small workloads"),
+        "split_cold_median_us": {
+            "store": round(float(np.median(cold_store_ms)) * 1e3, 2),
+            "attention_kernel": round(float(np.median(cold_kernel_ms)) * 1e3, 2),
+            "merge_and_launch_gaps": round((float(np.median(cold_decode_ms)) -
+                                            float(np.median(cold_kernel_ms))) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, kv_bytes),
+                     "bytes": "distinct K/V bytes (shared blocks once)" if args.shared_prefix else "logical K/V bytes",
+                     "algorithmic_bytes_per_launch": roof_bytes,
+                     "kernel": "decode_kernel (attention; excludes store and merge; with the shared-prefix option "
+                               "also its detection kernel)",
+                     "timing": "cold: mean of the K attention-kernel launches of the cold loop (HIP events on the "
+                               "library's stream), each after a 1 GiB read",
+                     "kernel_mean_ms": round(cold_mean, 5),
+                     "kernel_median_ms": round(float(np.median(cold_kernel_ms)), 5),
+                     "frac_of_stream_read": round(achieved / sr.ceiling_gbs, 4) if sr.ceiling_gbs else None,
+                     "stream_read_same_bytes": same,
+                     "time_frac_of_stream_read_same_bytes":
+                         round(same["median_us"] / (cold_mean * 1e3), 4) if same else None,
+                     "warm": {"achieved": round(warm_achieved, 2), "frac": round(warm_achieved / HBM_PEAK_GBS, 4),
+                              "kernel_mean_ms": round(warm_mean, 5),
+                              "note": "back-to-back launches of the warm loop: cache-assisted where the K/V "
+                                      "or part of it fits the 256 MB last-level cache"},
+                     "achieved_on_unique_bytes": round(x.unique_kv_bytes / (cold_mean * 1e-3) / 1e9, 2)},
+    }
+    if headline and not args.no_extra_timings:
+        calls = {"store": store, "decode": decode, "store_plus_decode": step}
+        for pz, nm in ((-2, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
+            calls[nm] = (lambda pz=pz: decode(None, pz, False))
+        calls["decode_balanced_shared_prefix"] = lambda: decode(None, -2, True)
+        timings = extra_timings(calls, 20)
+        timings["decode_tokens_per_s"] = round(cfg.batch / (timings["decode"]["median_us"] * 1e-6), 1)
+        timings["note"] = ("event pairs per call on the current stream, back to back (warm caches); "
+                           "decode includes the merge kernel where the plan splits")
+        rec["timings"] = timings
     if args.comparators:
-        print("[bench] comparator: torch gather-and-mask", file=sys.stderr, flush=True)
-        max_len = int(context_lens.max().item())
+        print(f"[bench] {name}: comparator torch gather-and-mask", file=sys.stderr, flush=True)
+        max_len = int(x.context_lens.max())
         ref = torch_gather_mask_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, max_len)
         torch.cuda.synchronize()
         reps = 3
@@ -627,63 +801,91 @@ def main():
             torch_gather_mask_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, max_len)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / reps
-        comparators = {"torch_gather_mask": {
+        rec["comparators"] = {"torch_gather_mask": {
             "ms_per_decode": round(ms, 4), "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
-            "speedup_of_library_kernel": round(ms / mean_kernel_ms, 2),
+            "speedup_of_library_kernel": round(ms / cold_mean, 2),
             "max_abs_diff_vs_library": float((ref - out).abs().max().item()),
             "note": "decode only (no store), fp32 math, padded to the longest context"}}
         del ref
-        torch.cuda.empty_cache()
-
-    # Per-call distributions, outside the timed region above. The store here rewrites the same
-    # slots with the same rows, so the cache contents do not change.
-    def decode_with(psize, shared=args.shared_prefix):
-        return lambda: pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
-                                                 partition_size=psize,
-                                                 cached_prefix_tokens=args.cached_prefix_tokens,
-                                                 shared_prefix=shared)
-    calls = {"store": lambda: pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache),
-             "decode": decode_with(args.partition_size), "store_plus_decode": step}
-    for psize, name in ((-2, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
-        calls[name] = decode_with(psize, False)
-    calls["decode_balanced_shared_prefix"] = decode_with(-2, True)
-    timings = None
-    if not args.no_extra_timings:
-        timings = extra_timings(calls, 20, 2 << 30, dev)
-        timings["decode_tokens_per_s"] = round(cfg.batch / (timings["decode"]["median_us"] * 1e-6), 1)
-        timings["note"] = ("cudaEvent pairs per call on the current stream, back to back (warm caches); "
-                           "decode includes the merge kernel where the plan splits")
-
-    traffic = traffic_from_profiles(cfg.name, kv_bytes)
-    result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the workload)",
-        "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
-                       partition_size=args.partition_size, shared_prefix=bool(args.shared_prefix),
-                       cached_prefix_tokens=args.cached_prefix_tokens or pa.DEFAULT_CACHED_PREFIX_TOKENS,
-                       launch="hip graph replay" if args.graph else "eager",
-                       step="pa_decode_step (fused scatter + attention)" if args.fused_step
-                       else "pa_store_kvcache + pa_paged_attention_decode", parallelism="single GPU"),
-        "tokens_per_s": round(cfg.batch / (ms_per_step * 1e-3), 1),
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(roof_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(roof_achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "bytes": roof_bytes,
-                     "achieved_on_logical_bytes": round(achieved, 2),
-                     "achieved_on_unique_bytes": round(achieved_unique, 2),
-                     "kernel": "decode_kernel (attention, excludes store and merge; with the shared-prefix "
-                               "option also its detection kernel)",
-                     "kernel_mean_ms": round(mean_kernel_ms, 5),
-                     "cold_kernel_median_ms": round(sorted(cold)[len(cold) // 2], 5) if cold else None},
-    }
-    if timings:
-        result["timings"] = timings
-    if comparators:
-        result["comparators"] = comparators
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(x, out.cpu().numpy(), args.cpu_budget_s)
+        print(f"[bench] {name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        budget = args.cpu_budget_s if headline else min(args.cpu_budget_s, 3.0)
+        one = 3.0 if name in ONE_THREAD_BASELINE else 0.0
+        rec["cpu_baseline"] = cpu_baseline(x, gpu_out, budget, one)
+    del k_cache, v_cache, q, k_new, v_new, block_tables, context_lens, slots, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = parse()
+    workload = args.workload or DEFAULT_WORKLOAD
+    if args.summarize_pmc:
+        print(summarize_pmc(workload, args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands))
+        return
+    if args.summarize_sq:
+        print(summarize_sq(workload, args.summarize_sq, args.sq_commands, "prefill" if args.prefill else "decode"))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(workload, args.summarize_trace, args.trace_command,
+                              "prefill" if args.prefill else "decode"))
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the library "
+              "has no cross-GPU step; each GPU would run its own shard of sequences or kv heads", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_attention_decode_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pa.load_library()
+    args.workload = workload
+    if args.prefill:
+        prefill_bench(args)
+        return
+    dev = torch.device("cuda:0")
+    sr = StreamRead(dev)
+    ceiling = None
+    if not args.no_extra_timings:
+        print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
+        ceiling = sr.ceiling()
+        sr.ceiling_gbs = ceiling["gbs"]
+
+    head = measure_workload(workload, args, dev, sr, headline=True)
+    records = {}
+    # Default run: the other workloads get records of their own in the same line.
+    if args.workload_given is False and not args.no_records:
+        for name in RECORD_WORKLOADS:
+            if name != workload:
+                records[name] = measure_workload(name, args, dev, sr, headline=False)
+
+    result = {
+        "metric": METRIC, "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": get_dtype(workload), "data": "synthetic (seeded, shapes of the workload)",
+        "config": dict(head["config"], parallelism="single GPU"),
+        "tokens_per_s": head["tokens_per_s"],
+        "pct_hbm_peak": round(100.0 * head["value"] / HBM_PEAK_GBS, 2),
+        "roofline": head["roofline"],
+    }
+    for key in ("cold_step", "split_cold_median_us", "timings", "comparators", "cpu_baseline"):
+        if key in head:
+            result[key] = head[key]
+    if ceiling:
+        result["stream_read_ceiling"] = ceiling
+    if records:
+        result["workloads"] = records
     print(json.dumps(result), flush=True)
+
+
+def get_dtype(name: str) -> str:
+    from workloads import get_config
+    return get_config(name).dtype
 
 
 if __name__ == "__main__":

@@ -2,7 +2,8 @@
 
 ``python -m paged_attention_decode_amd.build`` or ``build()`` from Python.
 Sources are compiled in parallel to objects under ``_build/`` and linked
-into ``paged_attention_decode_amd/libpagedattn.so``.
+into ``paged_attention_decode_amd/libpagedattn.so``; the benchmark's
+streaming-read kernel goes into its own ``libpa_stream_read.so``.
 """
 
 from __future__ import annotations
@@ -21,6 +22,9 @@ INCLUDE = ROOT / "include"
 BUILD = PKG / "_build"
 LIB = PKG / "libpagedattn.so"
 SOURCES = ["api.hip", "decode.hip", "prefill.hip", "store_kvcache.hip", "block_manager.cpp"]
+# Measurement-only library of the benchmark (streaming-read ceiling); not part of libpagedattn.
+STREAM_SOURCE = "stream_read.hip"
+STREAM_LIB = PKG / "libpa_stream_read.so"
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are kept out of the generated code. Matrix-core results stay in
@@ -53,13 +57,15 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, extra_flags=()) -> Path:
     hipcc = _hipcc()
     BUILD.mkdir(exist_ok=True)
-    objs = [BUILD / (Path(s).stem + ".o") for s in SOURCES]
-    cmds = [[hipcc, *COMMON, *extra_flags, "-c", str(CSRC / s), "-o", str(o)] for s, o in zip(SOURCES, objs)]
+    srcs = SOURCES + [STREAM_SOURCE]
+    objs = [BUILD / (Path(s).stem + ".o") for s in srcs]
+    cmds = [[hipcc, *COMMON, *extra_flags, "-c", str(CSRC / s), "-o", str(o)] for s, o in zip(srcs, objs)]
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB.with_suffix(".so.tmp")
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, objs), "-o", str(tmp)], verbose)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs[:-1]), (STREAM_LIB, objs[-1:])):
+        tmp = lib.with_suffix(".so.tmp")
+        _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, lib_objs), "-o", str(tmp)], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
