@@ -80,6 +80,10 @@ def parse():
                          "(full causal prefill); prints its own JSON line in TFLOP/s")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph instead of eager launches")
+    ap.add_argument("--graph-layers", type=int, default=0,
+                    help="time N decode steps, each on its own layer's caches (as one decode pass of an N-layer "
+                         "model), captured into one HIP graph, against the same N steps launched eagerly; "
+                         "prints its own JSON line")
     ap.add_argument("--comparators", action="store_true",
                     help="also time a PyTorch gather-and-mask decode on the same inputs (benchmark only)")
     ap.add_argument("--no-records", action="store_true",
@@ -98,6 +102,12 @@ def parse():
                     help="write profiles/decode_<workload>_kernel_trace.txt from a rocprofv3 --kernel-trace "
                          "--stats run of this script, then exit")
     ap.add_argument("--trace-command", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--summarize-latency", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/decode_<workload>_memory_latency.txt from rocprofv3 --pmc runs of "
+                         "TCC/TCP/TA/GRBM counters (read latency and reads in flight), then exit")
+    ap.add_argument("--summarize-graph-trace", metavar="TRACE_DIR",
+                    help="write profiles/graph_layers_<workload>_kernel_gaps.txt from a rocprofv3 --kernel-trace "
+                         "run of --graph-layers (per-pass span, busy time and gaps), then exit")
     ap.add_argument("--summarize-sq", nargs="+", metavar="PMC_DIR",
                     help="write profiles/<kernel>_<workload>_sq_counters.txt from rocprofv3 --pmc runs of SQ_ "
                          "counters (the attention kernel, or the prefill kernel with --prefill), then exit")
@@ -161,6 +171,11 @@ def kernel_source_sha(kernel: str = "decode") -> str:
     return hashlib.sha256(src.read_bytes()).hexdigest()
 
 
+def profile_name(workload: str, shared_prefix: bool = False) -> str:
+    """Workload part of a profile file name (runs with the shared-prefix option are kept apart)."""
+    return workload + ("_shared_prefix" if shared_prefix else "")
+
+
 def traffic_from_profiles(workload: str, launches_bytes: float):
     """HBM bytes per launch of the attention kernel from committed counter summaries, or None."""
     path = PROFILES / f"decode_{workload}_traffic.txt"
@@ -192,7 +207,7 @@ def _pmc_rows(directory: str, counter: str):
     return rows
 
 
-def summarize_pmc(workload: str, fetch_dir: str, write_dir: str, commands) -> Path:
+def summarize_pmc(workload: str, fetch_dir: str, write_dir: str, commands, shared_prefix: bool = False) -> Path:
     """HBM bytes per attention-kernel launch, with FETCH/WRITE_SIZE scaled by a copy of known size."""
     out = {}
     for key, directory, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
@@ -208,15 +223,16 @@ def summarize_pmc(workload: str, fetch_dir: str, write_dir: str, commands) -> Pa
     f_write = known_kib / out["write"][1]
     fetch_b = out["fetch"][0] * f_fetch * 1024.0
     write_b = out["write"][0] * f_write * 1024.0
-    path = PROFILES / f"decode_{workload}_traffic.txt"
+    path = PROFILES / f"decode_{profile_name(workload, shared_prefix)}_traffic.txt"
     PROFILES.mkdir(exist_ok=True)
+    opt = " --shared-prefix" if shared_prefix else ""
     path.write_text("\n".join([
-        f"# HBM traffic of the attention kernel (decode_kernel) on workload {workload}",
+        f"# HBM traffic of the attention kernel (decode_kernel) on workload {workload}{opt}",
         "# from two rocprofv3 --pmc runs of bench.py; FETCH_SIZE / WRITE_SIZE are KiB per dispatch,",
         f"# scaled by the same counter on a plain {COPY_BYTES >> 20} MiB copy kernel in the same run",
         f"# fetch command: {commands[0]}",
         f"# write command: {commands[1]}",
-        f"# summary command: python bench.py --workload {workload} --summarize-pmc {fetch_dir} {write_dir}",
+        f"# summary command: python bench.py --workload {workload}{opt} --summarize-pmc {fetch_dir} {write_dir}",
         f"kernel_source_sha256: {kernel_source_sha()}",
         f"decode_dispatches: {out['fetch'][2]}",
         f"fetch_kib_per_dispatch_raw: {out['fetch'][0]:.1f}",
@@ -278,6 +294,99 @@ def summarize_sq(workload: str, directories, commands, kernel: str = "decode") -
         simd_cycles = mean_ns * 1e-9 * 2.4e9 * 1024
         lines.append(f"mfma_busy_fraction_at_2.4GHz: {per('SQ_VALU_MFMA_BUSY_CYCLES') / simd_cycles:.3f}")
     path = PROFILES / f"{'prefill' if kernel == 'prefill' else 'decode'}_{workload}_sq_counters.txt"
+    PROFILES.mkdir(exist_ok=True)
+    path.write_text("\n".join(lines) + "\n")
+    return path
+
+
+def _counter_totals(directories, kernel_substr: str):
+    """Per counter: (sum over the kernel's dispatches, dispatch count), and the dispatches' mean duration."""
+    import csv
+    tot, disp, span = {}, {}, {}
+    for d in directories:
+        files = sorted(Path(d).rglob("*counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if kernel_substr not in r["Kernel_Name"]:
+                    continue
+                c = r["Counter_Name"]
+                tot[c] = tot.get(c, 0.0) + float(r["Counter_Value"])
+                disp.setdefault(c, set()).add((d, r["Dispatch_Id"]))
+                span[(d, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    per = {c: tot[c] / len(disp[c]) for c in tot}
+    mean_ns = sum(span.values()) / len(span) if span else 0.0
+    return tot, disp, per, mean_ns
+
+
+def summarize_latency(workload: str, directories, commands) -> Path:
+    """Memory-side view of the attention kernel: average L2->memory read latency (TCC EA read requests
+    in flight summed per cycle / requests), average CU->L2 read latency, reads in flight, TA busy."""
+    tot, disp, per, mean_ns = _counter_totals(directories, "decode_kernel")
+    if not tot:
+        raise SystemExit("no decode_kernel rows")
+    lines = [f"# memory latency counters of the decode_kernel kernel on workload {workload}, per dispatch",
+             *[f"# command: {c}" for c in commands],
+             f"# summary command: python bench.py --workload {workload} --summarize-latency {' '.join(directories)}",
+             f"kernel_source_sha256: {kernel_source_sha()}",
+             f"dispatch_mean_us: {mean_ns / 1e3:.2f}"]
+    for c in sorted(per):
+        lines.append(f"{c}: {per[c]:.6g} (mean of {len(disp[c])} dispatches)")
+    if per.get("TCC_EA0_RDREQ_sum") and per.get("TCC_EA0_RDREQ_LEVEL_sum") is not None:
+        lat = per["TCC_EA0_RDREQ_LEVEL_sum"] / per["TCC_EA0_RDREQ_sum"]
+        lines.append(f"l2_to_memory_read_latency_cycles: {lat:.0f}")
+        if per.get("GRBM_GUI_ACTIVE"):
+            lines.append(f"l2_to_memory_reads_in_flight_avg: {per['TCC_EA0_RDREQ_LEVEL_sum'] / per['GRBM_GUI_ACTIVE']:.0f}"
+                         " (per GPU cycle of the dispatch)")
+    if per.get("TCP_TCC_READ_REQ_sum") and per.get("TCP_TCC_READ_REQ_LATENCY_sum") is not None:
+        lines.append(f"cu_to_l2_read_latency_cycles: {per['TCP_TCC_READ_REQ_LATENCY_sum'] / per['TCP_TCC_READ_REQ_sum']:.0f}")
+    path = PROFILES / f"decode_{workload}_memory_latency.txt"
+    PROFILES.mkdir(exist_ok=True)
+    path.write_text("\n".join(lines) + "\n")
+    return path
+
+
+def summarize_graph_trace(workload: str, directory: str, command: str, layers: int, per_step: int) -> Path:
+    """Passes of `layers` decode steps (per_step library kernels each) in launch order: span from the
+    first kernel's start to the last one's end, summed kernel time, and the gaps between kernels."""
+    import csv
+    import numpy as np
+    traces = sorted(Path(directory).rglob("*kernel_trace.csv"))
+    if not traces:
+        raise SystemExit(f"no kernel_trace.csv under {directory}")
+    ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in csv.DictReader(open(traces[0]))
+                if "pa::" in r["Kernel_Name"])
+    n = layers * per_step
+    # graph_layers_bench's launch order: warm-up eager passes, 3 graph replays, then synchronised eager
+    # and graph passes, then back-to-back eager and graph passes (reps each)
+    import re
+    mw, ms = re.search(r"--warmup\s+(\d+)", command), re.search(r"--steps\s+(\d+)", command)
+    warm = max(1, int(mw.group(1))) if mw else 10
+    reps = max(3, int(ms.group(1))) if ms else 100
+    kinds = (["eager warm-up"] * warm + ["graph first replays"] * 3 + ["eager synchronised"] * reps +
+             ["graph synchronised"] * reps + ["eager back to back"] * reps + ["graph back to back"] * reps)
+    lines = [f"# library kernels of --graph-layers {layers} on workload {workload}, grouped into passes of {n}",
+             f"# kernels in launch order; the pass kinds follow the bench's fixed launch order",
+             f"# command: {command}",
+             f"# summary command: python bench.py --workload {workload} --graph-layers {layers} "
+             f"--summarize-graph-trace {directory}",
+             f"kernel_source_sha256: {kernel_source_sha()}",
+             f"{'pass':>4} {'kind':<20} {'span_us':>9} {'busy_us':>9} {'gap_median_us':>13} {'gap_max_us':>10}"]
+    by_kind = {}
+    for p in range(len(ks) // n):
+        seg = ks[p * n:(p + 1) * n]
+        gaps = np.array([seg[i + 1][0] - seg[i][1] for i in range(n - 1)]) / 1e3
+        kind = kinds[p] if p < len(kinds) else "?"
+        span, busy = (seg[-1][1] - seg[0][0]) / 1e3, sum(e - s for s, e in seg) / 1e3
+        by_kind.setdefault(kind, []).append((span, busy, float(np.median(gaps))))
+        lines.append(f"{p:>4} {kind:<20} {span:>9.1f} {busy:>9.1f} {float(np.median(gaps)):>13.2f} "
+                     f"{float(gaps.max()):>10.2f}")
+    for kind, v in by_kind.items():
+        a = np.array(v)
+        lines.append(f"mean {kind}: span {a[:, 0].mean():.1f} us, busy {a[:, 1].mean():.1f} us, "
+                     f"median gap {np.median(a[:, 2]):.2f} us; per layer step {a[:, 0].mean() / layers:.2f} us")
+    path = PROFILES / f"graph_layers_{workload}_kernel_gaps.txt"
     PROFILES.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")
     return path
@@ -725,6 +834,15 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
     cold_decode_ms = [c[1].elapsed_time(c[4]) for c in cev]
     gpu_out = out.cpu().numpy()
     same = sr.same_bytes(x.unique_kv_bytes if args.shared_prefix else x.kv_bytes) if sr.best else None
+    # A workload specified with its own launch mode is also timed, cold, in the library's automatic one.
+    auto_cold_ms = None
+    if psize != 0 and not args.no_extra_timings:
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+        for e in evs:
+            sr.flush()
+            decode(e, 0)
+        torch.cuda.synchronize()
+        auto_cold_ms = [b.elapsed_time(e) for b, e in evs]
 
     ms_per_step = wall * 1e3 / K
     kv_bytes = x.kv_bytes
@@ -761,7 +879,8 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
             "merge_and_launch_gaps": round((float(np.median(cold_decode_ms)) -
                                             float(np.median(cold_kernel_ms))) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, kv_bytes),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles(profile_name(name, args.shared_prefix), kv_bytes),
                      "bytes": "distinct K/V bytes (shared blocks once)" if args.shared_prefix else "logical K/V bytes",
                      "algorithmic_bytes_per_launch": roof_bytes,
                      "kernel": "decode_kernel (attention; excludes store and merge; with the shared-prefix option "
@@ -780,6 +899,15 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
                                       "or part of it fits the 256 MB last-level cache"},
                      "achieved_on_unique_bytes": round(x.unique_kv_bytes / (cold_mean * 1e-3) / 1e9, 2)},
     }
+    if auto_cold_ms:
+        am = float(np.mean(auto_cold_ms))
+        rec["roofline"]["automatic_mode"] = {
+            "partition_size": 0, "range_tokens": pa.decode_plan(
+                cfg.batch, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, int(x.block_tables.shape[1]),
+                {"fp32": 0, "fp16": 1, "bf16": 2}[cfg.dtype], 0, 0)["range_tokens"],
+            "kernel_mean_ms": round(am, 5), "achieved": round(roof_bytes / (am * 1e-3) / 1e9, 2),
+            "frac": round(roof_bytes / (am * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "the library's own choice for this batch (0 = automatic), cold, attention kernel only"}
     if headline and not args.no_extra_timings:
         calls = {"store": store, "decode": decode, "store_plus_decode": step}
         for pz, nm in ((-2, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
@@ -817,11 +945,120 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
     return rec
 
 
+def graph_layers_bench(args) -> None:
+    """N decode steps (store + attention (+ merge)) on N layers' own caches: eager launches against one
+    captured HIP graph replayed. Per-step times are wall clock over the whole pass / N."""
+    import numpy as np
+    import torch
+
+    import paged_attention_decode_amd as pa
+    from workloads import get_config, make_inputs
+
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.workload)
+    n = args.graph_layers
+    psize = args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(cfg.name, 0)
+    print(f"[bench] graph layers: generating {cfg.name}, {n} layers", file=sys.stderr, flush=True)
+    x = make_inputs(cfg)
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    k0 = _upload(x.k_cache, cfg.dtype, dev).view(
+        pa.k_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, tdt))
+    v0 = _upload(x.v_cache, cfg.dtype, dev).view(
+        pa.v_cache_shape(x.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.block_size))
+    layers = []
+    for _ in range(n):
+        layers.append({"k_cache": k0.clone(), "v_cache": v0.clone(),
+                       "q": _upload(x.q, cfg.dtype, dev), "k_new": _upload(x.k_new, cfg.dtype, dev),
+                       "v_new": _upload(x.v_new, cfg.dtype, dev),
+                       "out": torch.empty((cfg.batch, cfg.num_heads, cfg.head_dim), dtype=torch.float32,
+                                          device=dev)})
+    del k0, v0
+    block_tables = torch.from_numpy(x.block_tables).to(dev)
+    context_lens = torch.from_numpy(x.context_lens).to(dev)
+    slots = torch.from_numpy(x.slot_mapping).to(dev)
+    # the library's workspace, sized before capture (the graph records its address)
+    ws_bytes = pa.workspace_bytes(cfg.batch, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size,
+                                  int(x.block_tables.shape[1]), {"fp32": 0, "fp16": 1, "bf16": 2}[cfg.dtype], psize)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def one_pass():
+        for L in layers:
+            if args.fused_step:
+                pa.decode_step(L["q"], L["k_new"], L["v_new"], L["k_cache"], L["v_cache"], block_tables,
+                               context_lens, x.scale, L["out"], partition_size=psize, workspace=ws)
+            else:
+                pa.store_kvcache(L["k_new"], L["v_new"], slots, L["k_cache"], L["v_cache"])
+                pa.paged_attention_decode(L["q"], L["k_cache"], L["v_cache"], block_tables, context_lens, x.scale,
+                                          L["out"], partition_size=psize, workspace=ws)
+
+    for _ in range(max(1, args.warmup)):
+        one_pass()
+    torch.cuda.synchronize()
+    eager_ref = [L["out"].clone() for L in layers]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    same = all(bool(torch.equal(L["out"], r)) for L, r in zip(layers, eager_ref))
+
+    def timed(fn, reps):
+        walls = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
+        return float(np.median(walls))
+
+    reps = max(3, args.steps)
+    eager_s = timed(one_pass, reps)
+    graph_s = timed(graph.replay, reps)
+    # back to back, no synchronisation between passes: the steady state of a serving loop
+    k = max(3, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(k):
+        one_pass()
+    torch.cuda.synchronize()
+    eager_bb = (time.perf_counter() - t0) / k
+    t0 = time.perf_counter()
+    for _ in range(k):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_bb = (time.perf_counter() - t0) / k
+    kv = x.kv_bytes
+    print(json.dumps({
+        "metric": "decode step time in an N-layer pass, eager launches vs one captured HIP graph",
+        "value": round(graph_bb / n * 1e6, 2), "unit": "us per layer step (graph, back to back)",
+        "n_gpus": 1, "steps": reps, "warmup": args.warmup, "higher_is_better": False, "dtype": cfg.dtype,
+        "config": dict(describe(cfg), layers=n, partition_size=psize,
+                       step="pa_decode_step" if args.fused_step else "pa_store_kvcache + pa_paged_attention_decode"),
+        "graph_replay_matches_eager_bitwise": same,
+        "per_layer_step_us": {
+            "eager_back_to_back": round(eager_bb / n * 1e6, 2), "graph_back_to_back": round(graph_bb / n * 1e6, 2),
+            "eager_one_pass_synchronised": round(eager_s / n * 1e6, 2),
+            "graph_one_pass_synchronised": round(graph_s / n * 1e6, 2)},
+        "pass_us": {"eager_back_to_back": round(eager_bb * 1e6, 1), "graph_back_to_back": round(graph_bb * 1e6, 1)},
+        "kv_gbs_graph": round(kv * n / graph_bb / 1e9, 1), "kv_gbs_eager": round(kv * n / eager_bb / 1e9, 1)}),
+        flush=True)
+
+
 def main():
     args = parse()
     workload = args.workload or DEFAULT_WORKLOAD
     if args.summarize_pmc:
-        print(summarize_pmc(workload, args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands))
+        print(summarize_pmc(workload, args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands,
+                            args.shared_prefix))
+        return
+    if args.summarize_latency:
+        print(summarize_latency(workload, args.summarize_latency, args.sq_commands))
+        return
+    if args.summarize_graph_trace:
+        print(summarize_graph_trace(workload, args.summarize_graph_trace, args.trace_command, args.graph_layers,
+                                    1 if args.fused_step else 2))
         return
     if args.summarize_sq:
         print(summarize_sq(workload, args.summarize_sq, args.sq_commands, "prefill" if args.prefill else "decode"))
@@ -847,6 +1084,9 @@ def main():
     args.workload = workload
     if args.prefill:
         prefill_bench(args)
+        return
+    if args.graph_layers > 0:
+        graph_layers_bench(args)
         return
     dev = torch.device("cuda:0")
     sr = StreamRead(dev)
