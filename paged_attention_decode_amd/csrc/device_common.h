@@ -31,6 +31,7 @@ typedef __bf16 b8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef unsigned int u2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
 
 template <int DT, int D>
 struct Cfg {
@@ -51,12 +52,12 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// fp16 inputs: the softmax weights are computed times 2^kF16WeightLog2 (the same factor in the
-// running sum, so nothing else changes), which keeps them in fp16's normal range when they are
-// split into value + remainder for the second product. Unscaled, a weight below 2^-14 of the
-// running maximum would be an fp16 subnormal, with absolute precision 2^-25 only, and many such
-// weights could add up to a visible error. Decode weights are at most 1 before scaling
-// (2^15 after); prefill allows 2^8 (lazy rescale) and scales by 2^7.
+// fp16 inputs: the softmax weights are computed times 2^(15 - max_weight_log2) (the same factor
+// in the running sum, so nothing else changes), which keeps them in fp16's normal range when they
+// are rounded to fp16 for the second product (decode: value + remainder; prefill: one rounding).
+// Unscaled, a weight below 2^-14 of the running maximum would be an fp16 subnormal, with absolute
+// precision 2^-25 only, and many such weights could add up to a visible error. Decode weights are
+// at most 1 before scaling (2^15 after); prefill allows 2^8 (lazy rescale) and scales by 2^7.
 template <int DT>
 constexpr float weight_log2_scale(int max_weight_log2) {
   return DT == kF16 ? (float)(15 - max_weight_log2) : 0.0f;

@@ -23,9 +23,12 @@
 // instruction per 16 output rows. Its contraction index runs over the 32 keys
 // in the order (A: 4kq..4kq+3, B: 4kq..4kq+3) for lane group kq, which is the
 // order in which the first product leaves P in registers; V^T's operand takes
-// the same order from the two tiles' V loads. P enters as a sum of two 16-bit
-// parts, value + remainder: bf16 rounded to nearest (relative error <= 2^-16),
-// fp16 rounded toward zero by the packing conversion (< 2^-20).
+// the same order from the two tiles' V loads. For bf16, P enters as a sum of
+// two bf16 parts, value + remainder, each rounded to nearest (relative error
+// <= 2^-16). For fp16, P enters once, rounded to nearest (<= 2^-11), and the
+// softmax denominator sums those same rounded weights; one fp16 rounding keeps
+// the output within the tolerance with a wide margin, where one bf16 rounding
+// (2^-9) would not.
 //
 // K of the next step is requested as soon as this step's scores are issued,
 // V of the next step as soon as this step's second product is issued. Every
@@ -52,20 +55,6 @@ using namespace dev;
 constexpr int prefill_col_tiles(int dtype, int head_dim) {
   return dtype == kF32 ? (head_dim <= 64 ? 2 : 1)
                        : (head_dim <= 64 ? PA_PREFILL_NC64 : (head_dim <= 128 ? PA_PREFILL_NC128 : 1));
-}
-
-// p minus the fp16 value in the low (high) half of h, in one mixed-precision fma: the product
-// with -1 is exact and the sum is rounded once, so the result is the same as converting the
-// half to fp32 and subtracting, in one instruction instead of two.
-__device__ __forceinline__ float sub_f16_lo(float p, uint32_t h) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(p));
-  return r;
-}
-__device__ __forceinline__ float sub_f16_hi(float p, uint32_t h) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(p));
-  return r;
 }
 
 template <int DT, int D>
@@ -139,6 +128,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   }
 
   f4 acc[NC][C::kAcc];
+  f4 accl[NC];  // fp16: running sums of the rounded weights (matrix cores; every row the same)
   float m[NC], l[NC];
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
@@ -146,7 +136,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     l[ct] = 0.f;
 #pragma unroll
     for (int u = 0; u < C::kAcc; ++u) acc[ct][u] = f4{0.f, 0.f, 0.f, 0.f};
+    accl[ct] = f4{0.f, 0.f, 0.f, 0.f};
   }
+  // Matrix-core weight sums (fp16): an all-ones operand, kept in registers.
+  u4 ones_u = u4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  asm volatile("" : "+v"(ones_u));
+  const h8 ones8 = __builtin_bit_cast(h8, ones_u);
+  (void)ones8;
 
   const int64_t page_bytes = (int64_t)bs * D * C::kE;
   const int page_bytes32 = (int)page_bytes;
@@ -335,9 +331,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
         }
     } else if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-      for (int ct = 0; ct < NC; ++ct)
+      for (int ct = 0; ct < NC; ++ct) {
 #pragma unroll
         for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
+        accl[ct] *= alpha[ct];
+      }
     }
 
 #pragma unroll
@@ -345,7 +343,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m_use[ct]));
-      l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      // fp16: the running sum is taken over the rounded weights, on the matrix cores (below)
+      if constexpr (DT != kF16)
+        l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
       m[ct] = m_use[ct];
 
       if constexpr (DT == kF32) {
@@ -358,7 +358,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
           }
       } else {
         // P^T operand: slot j of lane group kq = key (j < 4 ? A : B) 4kq + (j & 3).
-        u4 ph, pl;
+        u4 ph, pl;  // pl: bf16 remainder parts
         if constexpr (DT == kBF16) {
           // gfx950 rounds two floats to bf16 (nearest even) in one instruction.
 #pragma unroll
@@ -370,14 +370,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
             pl[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf2));
           }
         } else {
+          // fp16: one part, rounded to nearest (relative error <= 2^-11). The running sum is of
+          // exactly these rounded weights, taken on the matrix cores (an all-ones row operand:
+          // every output row is the column's sum over the 32 keys, in fp32), so the
+          // normalisation matches the product: equal weights, or one dominant weight, give their
+          // values' mean exactly.
 #pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) {
-            const auto hv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2], p[2 * i2 + 1]);
-            const uint32_t hb = __builtin_bit_cast(uint32_t, hv);
-            const auto lv = __builtin_amdgcn_cvt_pkrtz(sub_f16_lo(p[2 * i2], hb), sub_f16_hi(p[2 * i2 + 1], hb));
-            ph[i2] = __builtin_bit_cast(uint32_t, hv);
-            pl[i2] = __builtin_bit_cast(uint32_t, lv);
-          }
+          for (int i2 = 0; i2 < 4; ++i2)
+            ph[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{p[2 * i2], p[2 * i2 + 1]}, hf2));
+          accl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, __builtin_bit_cast(h8, ph), accl[ct], 0, 0, 0);
         }
 #pragma unroll
         for (int w = 0; w < C::kLoads; ++w) {
@@ -389,12 +390,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
             acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, acc[ct][2 * w + 1], 0, 0, 0);
             acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc[ct][2 * w + 1], 0, 0, 0);
           } else {
-            const h8 hh8 = __builtin_bit_cast(h8, ph), hl8 = __builtin_bit_cast(h8, pl);
+            const h8 hh8 = __builtin_bit_cast(h8, ph);
             const h8 a0 = __builtin_bit_cast(h8, vr0[w]), a1 = __builtin_bit_cast(h8, vr1[w]);
             acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hh8, acc[ct][2 * w], 0, 0, 0);
-            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hl8, acc[ct][2 * w], 0, 0, 0);
             acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hh8, acc[ct][2 * w + 1], 0, 0, 0);
-            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hl8, acc[ct][2 * w + 1], 0, 0, 0);
           }
         }
       }
@@ -406,8 +405,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   // dim 32w + i and acc[2w + 1] row i = dim 32w + 16 + i. Lane (kq, ln) holds rows 4kq .. 4kq+3.
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
-    float lt = l[ct] + __shfl_xor(l[ct], 16);
-    lt += __shfl_xor(lt, 32);
+    float lt;
+    if constexpr (DT == kF16) {
+      lt = accl[ct][0];  // already summed over all keys (and lane groups) by the matrix cores
+    } else {
+      lt = l[ct] + __shfl_xor(l[ct], 16);
+      lt += __shfl_xor(lt, 32);
+    }
     const float inv = 1.0f / lt;
     if (!valid[ct]) continue;
     const int64_t base = ((int64_t)(q0 + qi[ct]) * a.num_heads + hh[ct]) * D;
@@ -585,6 +589,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
     }
   }
   f4 acc[NC][C::kAcc];
+  f4 accl[NC];  // fp16: running sums of the rounded weights (matrix cores; every row the same)
   float m[NC], l[NC];
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
@@ -592,7 +597,13 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
     l[ct] = 0.f;
 #pragma unroll
     for (int u = 0; u < C::kAcc; ++u) acc[ct][u] = f4{0.f, 0.f, 0.f, 0.f};
+    accl[ct] = f4{0.f, 0.f, 0.f, 0.f};
   }
+  // Matrix-core weight sums (fp16): an all-ones operand, kept in registers.
+  u4 ones_u = u4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  asm volatile("" : "+v"(ones_u));
+  const h8 ones8 = __builtin_bit_cast(h8, ones_u);
+  (void)ones8;
 
   const int64_t page_bytes = (int64_t)bs * D * C::kE;
   const int page_bytes32 = (int)page_bytes;
@@ -729,18 +740,22 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
       }
       if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct)
+        for (int ct = 0; ct < NC; ++ct) {
 #pragma unroll
           for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
+          accl[ct] *= alpha[ct];
+        }
       }
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m_use[ct]));
-        l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        // fp16: the running sum is taken over the rounded weights, on the matrix cores (below)
+        if constexpr (DT != kF16)
+          l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
         m[ct] = m_use[ct];
-        u4 ph, pl;
+        u4 ph, pl;  // pl: bf16 remainder parts
         if constexpr (DT == kBF16) {
 #pragma unroll
           for (int i2 = 0; i2 < 4; ++i2) {
@@ -751,14 +766,15 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
             pl[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf2));
           }
         } else {
+          // fp16: one part, rounded to nearest (relative error <= 2^-11). The running sum is of
+          // exactly these rounded weights, taken on the matrix cores (an all-ones row operand:
+          // every output row is the column's sum over the 32 keys, in fp32), so the
+          // normalisation matches the product: equal weights, or one dominant weight, give their
+          // values' mean exactly.
 #pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) {
-            const auto hv = __builtin_amdgcn_cvt_pkrtz(p[2 * i2], p[2 * i2 + 1]);
-            const uint32_t hb = __builtin_bit_cast(uint32_t, hv);
-            const auto lv = __builtin_amdgcn_cvt_pkrtz(sub_f16_lo(p[2 * i2], hb), sub_f16_hi(p[2 * i2 + 1], hb));
-            ph[i2] = __builtin_bit_cast(uint32_t, hv);
-            pl[i2] = __builtin_bit_cast(uint32_t, lv);
-          }
+          for (int i2 = 0; i2 < 4; ++i2)
+            ph[i2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{p[2 * i2], p[2 * i2 + 1]}, hf2));
+          accl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, __builtin_bit_cast(h8, ph), accl[ct], 0, 0, 0);
         }
 #pragma unroll
         for (int w = 0; w < C::kLoads; ++w) {
@@ -770,12 +786,10 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
             acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh, acc[ct][2 * w + 1], 0, 0, 0);
             acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc[ct][2 * w + 1], 0, 0, 0);
           } else {
-            const h8 hh8 = __builtin_bit_cast(h8, ph), hl8 = __builtin_bit_cast(h8, pl);
+            const h8 hh8 = __builtin_bit_cast(h8, ph);
             const h8 a0 = __builtin_bit_cast(h8, va0[w]), a1 = __builtin_bit_cast(h8, va1[w]);
             acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hh8, acc[ct][2 * w], 0, 0, 0);
-            acc[ct][2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, hl8, acc[ct][2 * w], 0, 0, 0);
             acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hh8, acc[ct][2 * w + 1], 0, 0, 0);
-            acc[ct][2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, hl8, acc[ct][2 * w + 1], 0, 0, 0);
           }
         }
       }
@@ -788,8 +802,13 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
   if (!active) return;
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
-    float lt = l[ct] + __shfl_xor(l[ct], 16);
-    lt += __shfl_xor(lt, 32);
+    float lt;
+    if constexpr (DT == kF16) {
+      lt = accl[ct][0];  // already summed over all keys (and lane groups) by the matrix cores
+    } else {
+      lt = l[ct] + __shfl_xor(l[ct], 16);
+      lt += __shfl_xor(lt, 32);
+    }
     const float inv = 1.0f / lt;
     if (!valid[ct]) continue;
     const int64_t base = ((int64_t)(q0 + qi[ct]) * a.num_heads + hh[ct]) * D;
