@@ -82,6 +82,7 @@ struct Plan {
   int n_hg = 0, gh_max = 0, segs_per_seq = 0;
   int casc_width = 0;  // shared-prefix window (0: off)
   int ws_cols = 0;     // partial-output columns per (range, slot)
+  int stash_slots = 0, stash_slot_floats = 0, stash_off = 0;  // deferred rows (split modes)
   int64_t whole_own_row = 0, whole_pre_row = 0;
   size_t off_lse = 0, off_meta = 0, off_meta_pre = 0, off_share = 0, ws_bytes = 0;
 };
@@ -176,6 +177,20 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
     p->lds += (size_t)num_seqs * sizeof(int32_t);
   }
   if (p->reduce) {
+    // Deferred rows: on gfx9-family GPUs a store counts in the same wait counter as the loads,
+    // so every later tile wait would also wait for the store to be acknowledged, which takes
+    // long under a full read stream. A wavefront therefore keeps the rows of its pieces in LDS
+    // slots after the prefix sums (header of 16 words, ws_cols rows of head_dim floats, their
+    // lse values) and writes them after its last tile; with no slot free it writes at once.
+    const size_t base = (p->lds + 15) & ~size_t(15);
+    const size_t slot_floats = 16 + (size_t)p->ws_cols * head_dim + (((size_t)p->ws_cols + 3) & ~size_t(3));
+    const size_t per_slot = (size_t)kWavesPerGroup * slot_floats * sizeof(float);
+    size_t slots = base < (size_t)kStashLdsBytes ? ((size_t)kStashLdsBytes - base) / per_slot : 0;
+    if (slots > (size_t)kMaxStashSlots) slots = kMaxStashSlots;
+    p->stash_slots = (int)slots;
+    p->stash_slot_floats = (int)slot_floats;
+    p->stash_off = (int)(base / sizeof(float));
+    if (slots > 0) p->lds = base + slots * per_slot;
     if (p->range_tiles == 0 || p->num_ranges < p->num_waves) p->num_ranges = p->num_waves;
     const size_t windows = p->casc_width > 0 ? ((size_t)num_seqs + p->casc_width - 1) / p->casc_width : 0;
     // Rows of pieces cut by range boundaries; with shared prefixes also rows for whole segments
@@ -509,6 +524,9 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
   a.ws_meta_pre = (ws && p.casc_width > 0) ? reinterpret_cast<int4*>(ws + p.off_meta_pre) : nullptr;
   a.ws_share = (ws && p.casc_width > 0) ? reinterpret_cast<int32_t*>(ws + p.off_share) : nullptr;
   a.ws_cols = p.ws_cols;
+  a.stash_slots = p.stash_slots;
+  a.stash_slot_floats = p.stash_slot_floats;
+  a.stash_off = p.stash_off;
   a.whole_own_row = p.whole_own_row;
   a.whole_pre_row = p.whole_pre_row;
   // A prefix piece addresses the query rows of a whole window from one buffer resource.

@@ -13,7 +13,10 @@
 // number of KV bytes however skewed the lengths are. A segment that lies
 // inside one range is finished by its wavefront (output written directly);
 // a segment cut by range boundaries leaves one normalised partial output and
-// its log2-sum-exp2 per piece, merged afterwards by reduce_kernel.
+// its log2-sum-exp2 per piece, merged afterwards by reduce_kernel. A wavefront
+// keeps the rows it finishes in LDS and writes them after its last tile: on
+// gfx9-family GPUs a store shares the wait counter of the loads, and waiting
+// for its acknowledgement behind a full read stream would stall the next tiles.
 //
 // Shared prefixes (an option; prefix caching shares the physical blocks of a
 // common prefix between sequences): share_kernel finds, per window of 16/G
@@ -58,10 +61,12 @@ struct Piece {
   // cols != 0: a shared prefix. The tiles are read through sequence s's block table, and the
   // columns are the kv head's query heads of the sequences win + m for each bit m of cols
   // (column m * group + head); the result always goes to the workspace, all 16 columns.
+  // stash != null: the rows are not written here but left in that LDS slot (header words 0-5,
+  // values from float 16, lse values after the rows), and write_stashed writes them later.
   static __device__ __forceinline__ void run(const DecodeArgs& a, int s, int r, int L, int lt0, int lt1,
                                              bool complete, int64_t row_base, int lane,
                                              float* part_o = nullptr, float* part_lse = nullptr,
-                                             int win = 0, int cols = 0) {
+                                             int win = 0, int cols = 0, float* stash = nullptr) {
     // All of these are the same in every lane. Saying so lets the compiler keep what derives
     // from them in scalar registers, and read the block table with scalar loads.
     s = __builtin_amdgcn_readfirstlane(s);
@@ -368,9 +373,40 @@ struct Piece {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = (L > 0) ? 1.0f / lt : 0.0f;
+    f4 v[C::kAcc];
+#pragma unroll
+    for (int u = 0; u < C::kAcc; ++u) v[u] = acc[u] * inv;
+    if (stash != nullptr) {
+      // Rows (row0 + column) of `out` (complete) or of the workspace; every lane writes the same
+      // header words and later reads back only what it wrote itself.
+      const uint64_t vmask = __ballot(valid);
+      const int64_t row0 = complete ? (int64_t)s * a.num_heads + h0 : row_base;
+      int* hdr = reinterpret_cast<int*>(stash);
+      hdr[0] = (int)row0;
+      hdr[1] = (int)(row0 >> 32);
+      hdr[2] = (int)vmask;
+      hdr[3] = (int)(vmask >> 32);
+      hdr[4] = complete ? 1 : 0;
+      if (!valid) return;
+      // Row-major: column ln's row at float 16 + ln * D, in dim order, so that write_stashed
+      // writes whole rows with consecutive lanes on consecutive 16-byte chunks.
+      float* rowp = stash + 16 + ln * D;
+      if constexpr (DT == kF32) {
+#pragma unroll
+        for (int u = 0; u < C::kAcc; ++u) *reinterpret_cast<f4*>(rowp + 16 * u + 4 * kq) = v[u];
+      } else {
+#pragma unroll
+        for (int w = 0; w < C::kLoads; ++w) {
+          *reinterpret_cast<f4*>(rowp + 32 * w + 8 * kq) = f4{v[2 * w][0], v[2 * w + 1][0], v[2 * w][1], v[2 * w + 1][1]};
+          *reinterpret_cast<f4*>(rowp + 32 * w + 8 * kq + 4) =
+              f4{v[2 * w][2], v[2 * w + 1][2], v[2 * w][3], v[2 * w + 1][3]};
+        }
+      }
+      if (kq == 0 && !complete) stash[16 + a.ws_cols * D + ln] = m + __log2f(lt);
+      return;
+    }
     if (!valid) return;
 
-    float* dst_f32 = nullptr;
     void* dst = a.out;
     int64_t base;
     bool as_f32 = a.out_f32 != 0;
@@ -383,28 +419,65 @@ struct Piece {
       if (kq == 0) part_lse[ln] = m + __log2f(lt);
     } else {
       const int64_t row = row_base + ln;
-      dst_f32 = a.ws_o;
-      dst = dst_f32;
+      dst = a.ws_o;
       base = row * D;
       as_f32 = true;
       if (kq == 0) a.ws_lse[row] = m + __log2f(lt);
     }
+    write_row(dst, base, as_f32, v, kq);
+  }
+
+  // One lane's share of a head row: normalised O^T tile values v, written from element `base`
+  // of dst in fp32 or (as_f32 false) in the input dtype.
+  static __device__ __forceinline__ void write_row(void* dst, int64_t base, bool as_f32, const f4 (&v)[C::kAcc],
+                                                   int kq) {
     if constexpr (DT == kF32) {
       // O^T tile u holds dims 16u + 4kq + r.
 #pragma unroll
-      for (int u = 0; u < C::kAcc; ++u) {
-        f4 v = acc[u] * inv;
-        *reinterpret_cast<f4*>(reinterpret_cast<float*>(dst) + base + 16 * u + 4 * kq) = v;
-      }
+      for (int u = 0; u < C::kAcc; ++u)
+        *reinterpret_cast<f4*>(reinterpret_cast<float*>(dst) + base + 16 * u + 4 * kq) = v[u];
     } else {
       // O^T tiles 2w (even dims) and 2w+1 (odd dims) hold dims 32w + 8kq + 2r + parity.
 #pragma unroll
       for (int w = 0; w < C::kLoads; ++w) {
-        float v[8];
+        float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = acc[2 * w + (j & 1)][j >> 1] * inv;
-        store8<DT>(dst, base + 32 * w + 8 * kq, v, as_f32);
+        for (int j = 0; j < 8; ++j) x[j] = v[2 * w + (j & 1)][j >> 1];
+        store8<DT>(dst, base + 32 * w + 8 * kq, x, as_f32);
       }
+    }
+  }
+
+  // Writes the rows and segment records that run left in `used` LDS slots: each row in order,
+  // consecutive lanes on consecutive 16-byte chunks.
+  static __device__ __forceinline__ void write_stashed(const DecodeArgs& a, const float* slots, int used, int lane) {
+    constexpr int kChunks = D / 4;  // 16-byte chunks of fp32 per row
+    const int cols = a.ws_cols;
+    for (int k = 0; k < used; ++k) {
+      const float* sl = slots + (int64_t)k * a.stash_slot_floats;
+      const int* hdr = reinterpret_cast<const int*>(sl);
+      const uint64_t meta = (uint64_t)(uint32_t)hdr[6] | ((uint64_t)(uint32_t)hdr[7] << 32);
+      if (meta != 0 && lane == 0) *reinterpret_cast<int4*>(meta) = make_int4(hdr[8], hdr[9], hdr[10], hdr[11]);
+      const uint64_t vmask = (uint64_t)(uint32_t)hdr[2] | ((uint64_t)(uint32_t)hdr[3] << 32);
+      const int64_t row0 = (int64_t)(uint32_t)hdr[0] | ((int64_t)hdr[1] << 32);
+      const bool complete = hdr[4] != 0;
+      // Output rows of fp32 inputs are always fp32; workspace rows are fp32.
+      const bool as_f32 = !complete || a.out_f32 != 0 || DT == kF32;
+      void* dst = complete ? a.out : static_cast<void*>(a.ws_o);
+      for (int i = lane; i < cols * kChunks; i += 64) {
+        const int c = i / kChunks;
+        if (!((vmask >> c) & 1)) continue;
+        const int d = (i - c * kChunks) * 4;
+        const f4 x = *reinterpret_cast<const f4*>(sl + 16 + c * D + d);
+        const int64_t o = (row0 + c) * D + d;
+        if (as_f32) {
+          *reinterpret_cast<f4*>(reinterpret_cast<float*>(dst) + o) = x;
+        } else {
+          const float y[4] = {x[0], x[1], x[2], x[3]};
+          store4<DT>(dst, o, y, false);
+        }
+      }
+      if (!complete && lane < cols && ((vmask >> lane) & 1)) a.ws_lse[row0 + lane] = sl[16 + cols * D + lane];
     }
   }
 };
@@ -419,7 +492,7 @@ template <int DT, int D, bool FUSE, bool SHARED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   // Split modes: [num_seqs + 1], the first global tile of each sequence. Workgroup split: the
   // partial rows of the segment being merged.
-  extern __shared__ int32_t s_prefix[];
+  extern __shared__ __align__(16) int32_t s_prefix[];
   __shared__ int32_t s_wsum[kWavesPerGroup];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -566,6 +639,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   // balanced mode there are at most as many ranges as wavefronts; a fixed range size can
   // need more, and then each wavefront takes every num_waves-th range.
   const int nranges = (total + R - 1) / R;
+  // This wavefront's LDS slots for finished rows, written after its last tile.
+  float* const slots = reinterpret_cast<float*>(s_prefix) + a.stash_off +
+                       __builtin_amdgcn_readfirstlane(tid >> 6) * a.stash_slots * a.stash_slot_floats;
+  int used = 0;
   for (int rho = wave; rho < nranges; rho += a.num_waves) {
     int t = rho * R;
     const int t_end = min(total, t + R);
@@ -607,10 +684,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       int64_t row_base = ((int64_t)rho * 2 + slot) * a.ws_cols;
       if (whole && in_pre) row_base = a.whole_pre_row + ((int64_t)(s / CW) * H + r) * kHeadsPerTile;
       else if (whole) row_base = a.whole_own_row + ((int64_t)s * H + r) * a.gh_max;
-      if (lt == 0 && lane == 0) {
+      float* stash = used < a.stash_slots ? slots + used * a.stash_slot_floats : nullptr;
+      if (lt == 0) {
         // This range holds the segment's first piece: record where all pieces are.
         int4* meta = in_pre ? a.ws_meta_pre + (int64_t)(s / CW) * H + r : a.ws_meta + (int64_t)s * H + r;
-        *meta = make_int4(rho, slot, (t + tiles - 1) / R, 0);
+        const int4 mv = make_int4(rho, slot, (t + tiles - 1) / R, 0);
+        if (stash != nullptr) {
+          int* hdr = reinterpret_cast<int*>(stash);
+          hdr[6] = (int)(uint32_t)reinterpret_cast<uint64_t>(meta);
+          hdr[7] = (int)(reinterpret_cast<uint64_t>(meta) >> 32);
+          hdr[8] = mv.x;
+          hdr[9] = mv.y;
+          hdr[10] = mv.z;
+          hdr[11] = mv.w;
+        } else if (lane == 0) {
+          *meta = mv;
+        }
+      } else if (stash != nullptr) {
+        int* hdr = reinterpret_cast<int*>(stash);
+        hdr[6] = 0;
+        hdr[7] = 0;
       }
       int win = 0, cols = 0, p_len = L, p_lt0 = skip + lt;
       if (in_pre) {
@@ -622,7 +715,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
         p_lt0 = lt;
       }
       Piece<DT, D, FUSE>::run(a, s, r, p_len, p_lt0, p_lt0 + n, complete, row_base, lane, nullptr, nullptr,
-                              win, cols);
+                              win, cols, stash);
+      used += stash != nullptr ? 1 : 0;
       t += n;
       if (t >= t_end) break;
       first = false;
@@ -639,6 +733,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
       }
     }
   }
+  Piece<DT, D, FUSE>::write_stashed(a, slots, used, lane);
 }
 
 // Shared-prefix detection. Sequences are taken in windows of CW = casc_width consecutive ones

@@ -21,6 +21,10 @@ constexpr int kHeadsPerTile = 16;
 constexpr int kMaxSeqs = 16383;
 // Largest batch for shared-prefix decode: the per-sequence sharing words also live in LDS.
 constexpr int kMaxSharedSeqs = 8191;
+// Split modes: LDS a workgroup may use for the prefix sums plus the deferred-row slots, and the
+// most slots per wavefront.
+constexpr int kStashLdsBytes = 65536;
+constexpr int kMaxStashSlots = 8;
 // Shared-prefix word of a sequence (0: the sequence reads its whole context itself):
 // bits 0-15 the prefix length in 16-token tiles, bits 16-19 the window slot of the group's
 // leader (whose block table the prefix is read through), bit 20 set.
@@ -75,6 +79,12 @@ struct DecodeArgs {
   int32_t cached_prefix_tokens;  // tiles starting before this token use cached loads, later ones stream
   int32_t ws_cols;        // partial-output columns per (range, slot): gh_max, or 16 with shared prefixes
   int32_t casc_width;     // sequences per shared-prefix window (16 / group), 0 = no prefix sharing
+  // Split modes: LDS slots per wavefront that hold finished rows until its last tile is done
+  // (0: rows are written at once), their size in floats, and where the slots start (floats from
+  // the start of the dynamic LDS).
+  int32_t stash_slots;
+  int32_t stash_slot_floats;
+  int32_t stash_off;
   // Fused scatter of the step's token at position L-1 (null: plain decode).
   const void* k_new;      // [num_seqs][num_kv_heads][head_dim]
   const void* v_new;
