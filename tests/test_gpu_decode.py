@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import CONFIG_ORDER, get_config, make_inputs, nan_of, poison_blocks
+from workloads import CONFIG_ORDER, get_config, make_inputs, nan_of, poison_blocks, to_storage
 from _gpu_helpers import (TOL, custom_config, geometry, half_ulp, np_to_torch, oracle_after_store, to_device,
                           torch_dtype, torch_to_np)
 
@@ -414,25 +414,41 @@ def test_fused_step_full_configs(cuda, name, psize):
     _fused_vs_two_calls(cuda, x, psize)
 
 
-def _tiny_weight_case(length=16384, d=64, bs=16):
-    """fp16, one sequence, G = 1: key 0 dominates and every other key has weight ~2^-15 of it, all
+def _tiny_weight_case(length=16384, d=64, bs=16, dtype="fp16"):
+    """One sequence, G = 1: key 0 dominates and every other key has weight ~2^-15 of it, all
     with the same value sign, so rounding errors on the small weights add up in one direction.
     Built with the oracle's own scatter on a shuffled block table."""
-    geo = oracle.CacheGeometry(num_blocks=length // bs + 8, num_kv_heads=1, head_dim=d, block_size=bs, dtype="fp16")
+    geo = oracle.CacheGeometry(num_blocks=length // bs + 8, num_kv_heads=1, head_dim=d, block_size=bs, dtype=dtype)
     rng = np.random.default_rng(2024)
-    q = np.zeros((1, 1, d), np.float16)
+    q = np.zeros((1, 1, d), np.float32)
     q[0, 0, 0] = 8.0
-    k = np.zeros((length, 1, d), np.float16)
-    k[0, 0, 0] = 10.3984375                 # scale 1/8: logit gap 10.398 = 15.0 in log2 units
-    v = np.full((length, 1, d), 4.0, np.float16)
+    k = np.zeros((length, 1, d), np.float32)
+    k[0, 0, 0] = 10.3984375                 # scale 1/8: logit gap 10.398 = 15.0 in log2 units (fp16)
+    v = np.full((length, 1, d), 4.0, np.float32)
     v[0] = -4.0
-    v[1:, 0, :] += rng.integers(0, 8, (length - 1, d)).astype(np.float16) * np.float16(0.125)
+    v[1:, 0, :] += rng.integers(0, 8, (length - 1, d)).astype(np.float32) * np.float32(0.125)
+    q, k, v = (to_storage(a, dtype) for a in (q, k, v))
     blocks = rng.permutation(geo.num_blocks)[:length // bs].astype(np.int32)
     slots = (blocks[np.arange(length) // bs] * bs + np.arange(length) % bs).astype(np.int32)
-    kc = np.zeros(int(np.prod(geo.k_shape)), np.float16)
-    vc = np.zeros(int(np.prod(geo.v_shape)), np.float16)
+    kc = np.zeros(int(np.prod(geo.k_shape)), k.dtype)
+    vc = np.zeros(int(np.prod(geo.v_shape)), v.dtype)
     kc, vc = oracle.store_kvcache(k, v, slots, kc, vc, geo)
     return geo, q, kc, vc, blocks[None, :], np.array([length], np.int32)
+
+
+def _one_rounding_bound(geo, q, kc, vc, bt, cl):
+    """Bound of a one-token prefill that rounds each weight once to fp16: weights in units of the
+    dominant one's (2^7, exact) are p = 2^7 * exp(scale * (0 - q.k0)) for the n small keys, each
+    rounded to fp16 (error <= half an ulp, all in one direction). With S = the sum of their values
+    per dim, out = (2^7 v0 + p S) / (2^7 + n p) moves by 2^7 (S - n v0) / (2^7 + n p)^2 per unit of
+    p. Plus 1e-4 for fp32 accumulation."""
+    n = int(cl[0]) - 1
+    k, v = oracle.gather_kv(kc, vc, bt[0], int(cl[0]), geo)
+    v0, S = v[0, 0], v[1:, 0].sum(axis=0)
+    qk0 = float(oracle.widen(q, geo.dtype)[0, 0] @ k[0, 0])
+    p = 2.0 ** 7 * np.exp(float(np.float32(0.125)) * (0.0 - qk0))
+    half_ulp_p = 2.0 ** (np.floor(np.log2(p)) - 11)
+    return 2.0 ** 7 * np.abs(S - n * v0) / (2.0 ** 7 + n * p) ** 2 * half_ulp_p + 1e-4
 
 
 def test_fp16_many_tiny_weights_keep_their_precision(cuda):
@@ -464,15 +480,8 @@ def test_fp16_many_tiny_weights_keep_their_precision(cuda):
     torch.cuda.synchronize()
     err = np.abs(pre.cpu().numpy() - ref[0])[0]
     _say(f"[gpu] tiny fp16 weights, one-token prefill: max-abs error {err.max():.2e}")
-    # Weights in units of the dominant one's (2^7, exact): p = 2^7 * exp(scale * (0 - q.k0)) for
-    # the n small keys, rounded once to fp16 (error <= half an ulp, all in one direction). With
-    # S = sum of their values per dim, out = (2^7 v0 + p S) / (2^7 + n p) moves by
-    # 2^7 (S - n v0) / (2^7 + n p)^2 per unit of p.
-    n = int(cl[0]) - 1
-    _, v = oracle.gather_kv(kc, vc, bt[0], int(cl[0]), geo)
-    v0, S = v[0, 0], v[1:, 0].sum(axis=0)
-    p = 2.0 ** 7 * np.exp(float(np.float32(0.125)) * (0.0 - 8.0 * 10.3984375))
-    half_ulp_p = 2.0 ** (np.floor(np.log2(p)) - 11)
-    bound = 2.0 ** 7 * np.abs(S - n * v0) / (2.0 ** 7 + n * p) ** 2 * half_ulp_p + 1e-4
+    bound = _one_rounding_bound(geo, q, kc, vc, bt, cl)
     assert (err <= bound).all(), (err.max(), bound.min())
     assert bound.max() < 1e-3  # well inside the 2e-3 parity tolerance
+
+
