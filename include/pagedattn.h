@@ -161,9 +161,12 @@ int pa_paged_attention_decode(const void* q, const void* k_cache, const void* v_
  * Options for pa_paged_attention_decode_ex.
  *
  * partition_size (tokens):
- *    0  automatic: one pass (-1) when no context can exceed 512 tokens
- *       (max_blocks_per_seq * block_size <= 512), balanced ranges (-2)
- *       otherwise. Decided on the host from the sizes alone.
+ *    0  automatic: when no context can exceed 512 tokens
+ *       (max_blocks_per_seq * block_size <= 512), the workgroup split (-3) if
+ *       every (sequence, kv head, head group) context gets a resident
+ *       workgroup of its own (at most 2 * compute units of them), else one
+ *       pass (-1); balanced ranges (-2) otherwise. Decided on the host from
+ *       the sizes alone.
  *   -1  one pass: every (sequence, kv head) context is handled whole by one
  *       wavefront; no reduce kernel runs.
  *   -2  balanced ranges: the concatenated 16-token tiles of all (sequence,

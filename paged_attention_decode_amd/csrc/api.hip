@@ -123,12 +123,18 @@ int make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t
   const int64_t upper_tiles = segs * (max_tiles > 0 ? max_tiles : 1);
   const int64_t resident = (int64_t)num_cus * kGroupsPerCU * kWavesPerGroup;
   int64_t waves;
-  // Automatic: one pass when no context can be longer than kOnePassMaxTokens (the host's bound,
-  // max_blocks * block_size; it reads no device memory): every segment is then short, one
-  // wavefront per segment finishes about as soon as balanced ranges would, and no merge kernel
-  // runs. Otherwise balanced ranges.
-  if (partition_size == 0)
-    partition_size = (int64_t)max_blocks * block_size <= kOnePassMaxTokens ? -1 : kBalanced;
+  // Automatic: when no context can be longer than kOnePassMaxTokens (the host's bound,
+  // max_blocks * block_size; it reads no device memory) every segment is short and no merge
+  // kernel is needed. Then, if every segment gets a resident workgroup of its own, the workgroup
+  // split puts four wavefronts on each segment's chain of dependent loads; with more segments
+  // one wavefront per segment (one pass), since the split would leave three of four wavefronts
+  // idle on one-tile segments. Otherwise balanced ranges.
+  if (partition_size == 0) {
+    if ((int64_t)max_blocks * block_size <= kOnePassMaxTokens)
+      partition_size = segs <= resident / kWavesPerGroup ? kWorkgroupSplit : -1;
+    else
+      partition_size = kBalanced;
+  }
   // Workgroup split keeps four partial outputs and their log-sum-exps in LDS; where they would
   // not fit in 64 KiB (head_dim 256 with 16 heads per group) it runs as one pass.
   const size_t split_lds = (size_t)kWavesPerGroup * p->gh_max * (head_dim + 1) * sizeof(float);

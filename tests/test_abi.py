@@ -124,6 +124,16 @@ def test_plan_automatic_takes_one_pass_for_short_bounded_contexts(mb, bs, one_pa
     assert forced["range_tokens"] == 0 and forced["uses_reduce"]
 
 
+@pytest.mark.parametrize("num_seqs,expect", [(60, -3), (64, -3), (65, -1), (2048, -1)])
+def test_plan_automatic_short_contexts_split_in_workgroups_while_they_fit(num_seqs, expect):
+    # 8 kv heads: 64 sequences give 512 segments, one resident workgroup each on 256 CUs (2 per CU)
+    p = _plan(num_seqs=num_seqs, max_blocks_per_seq=2, block_size=256)
+    assert p["range_tokens"] == expect and not p["uses_reduce"] and p["workspace_bytes"] == 0
+    # where four partial rows would not fit in LDS (head_dim 256, 16 heads per kv head) it is one pass
+    q = _plan(num_seqs=8, num_heads=32, num_kv_heads=2, head_dim=256, max_blocks_per_seq=2, block_size=256)
+    assert q["range_tokens"] == -1
+
+
 def test_plan_large_head_groups_split_into_sixteen():
     p = _plan(num_heads=40, num_kv_heads=2, partition_size=-1)
     assert p["num_waves"] == min(256 * 2 * 2, 256 * 8)
