@@ -392,16 +392,18 @@ def summarize_graph_trace(workload: str, directory: str, command: str, layers: i
     return path
 
 
-def summarize_trace(workload: str, directory: str, command: str, kernel: str = "decode") -> Path:
+def summarize_trace(workload: str, directory: str, command: str, kernel: str = "decode",
+                    shared_prefix: bool = False) -> Path:
     """Per-kernel duration statistics of a rocprofv3 --kernel-trace --stats run, as text."""
     import csv
     files = sorted(Path(directory).rglob("*kernel_stats.csv"))
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {directory}")
-    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+    opt = " --shared-prefix" if shared_prefix else ""
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}{opt}",
              f"# command: {command}",
-             f"# summary command: python bench.py --workload {workload} {'--prefill ' if kernel == 'prefill' else ''}"
-             f"--summarize-trace {directory}",
+             f"# summary command: python bench.py --workload {workload}{opt} "
+             f"{'--prefill ' if kernel == 'prefill' else ''}--summarize-trace {directory}",
              f"kernel_source_sha256: {kernel_source_sha(kernel)}",
              f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
     for r in csv.DictReader(open(files[0])):
@@ -423,7 +425,7 @@ def summarize_trace(workload: str, directory: str, command: str, kernel: str = "
         if timed:
             lines.append(f"timed_launches: {len(timed)} (the last --steps launches of the {main_name} kernel)")
             lines.append(f"timed_launches_mean_us: {sum(timed) / len(timed) / 1e3:.2f}")
-    path = PROFILES / f"{kernel}_{workload}_kernel_trace.txt"
+    path = PROFILES / f"{kernel}_{profile_name(workload, shared_prefix)}_kernel_trace.txt"
     PROFILES.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")
     return path
@@ -1065,7 +1067,7 @@ def main():
         return
     if args.summarize_trace:
         print(summarize_trace(workload, args.summarize_trace, args.trace_command,
-                              "prefill" if args.prefill else "decode"))
+                              "prefill" if args.prefill else "decode", args.shared_prefix))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
