@@ -306,32 +306,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
           if (t > pos[ct]) x[ct][j] = -INFINITY;
         }
     }
-    float m_use[NC], alpha[NC];
-    bool moved = false;
+    // The running maximum m of each column is kept unless a score exceeds it by more than 8
+    // (log2 units): weights stay below 2^8, and the accumulators are rescaled only on such
+    // jumps. Each lane tests its own scores against m + 8 (c > 0, and rounding keeps the order,
+    // so a lane's maximum times c exceeds m + 8 exactly when the column's does); only when some
+    // lane finds a jump is the maximum over the column's rows taken. That happens on an item's
+    // first step (m = -inf; key 0 is visible to every column, so m is finite afterwards) and on
+    // real jumps. Columns without a jump keep alpha = 1.
+    float alpha[NC];
+    bool jump = false;
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
+      alpha[ct] = 1.0f;
       // IEEE-2019 maximum: gfx950 has a three-input form, and it needs no NaN quieting first.
-      const float mt = max_over_rows(fmax8(x[ct]));
-      // Key 0 is visible to every column, so m is finite from the first step on. The running
-      // maximum is kept unless it grew by more than 8 (log2 units): weights stay below 2^8,
-      // and the accumulators are rescaled only on such jumps instead of on every new maximum.
-      const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
-      m_use[ct] = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
-      alpha[ct] = exp2_fast(m[ct] - m_use[ct]);
-      moved = moved || alpha[ct] != 1.0f;
+      jump = jump || fmax8(x[ct]) * c > m[ct] + 8.0f;
     }
-    if constexpr (DT == kBF16 && NC > 2) {
-      // One rescale branch per tile here: with a single branch for all four tiles this instance
-      // needs more than 256 VGPRs (two wavefronts per SIMD no longer fit).
-#pragma unroll
-      for (int ct = 0; ct < NC; ++ct)
-        if (__builtin_amdgcn_ballot_w64(alpha[ct] != 1.0f) != 0) {
-#pragma unroll
-          for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
-        }
-    } else if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+    if (__builtin_amdgcn_ballot_w64(jump) != 0) {
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
+        const float mt = max_over_rows(fmax8(x[ct]));
+        const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
+        const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
+        alpha[ct] = exp2_fast(m[ct] - m_use);
+        m[ct] = m_use;
 #pragma unroll
         for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
         accl[ct] *= alpha[ct];
@@ -342,11 +339,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     for (int ct = 0; ct < NC; ++ct) {
       float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m_use[ct]));
+      for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m[ct]));
       // fp16: the running sum is taken over the rounded weights, on the matrix cores (below)
       if constexpr (DT != kF16)
         l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-      m[ct] = m_use[ct];
 
       if constexpr (DT == kF32) {
 #pragma unroll
@@ -727,20 +723,23 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
             if (t > pos[ct]) x[ct][j] = -INFINITY;
           }
       }
-      float m_use[NC], alpha[NC];
-      bool moved = false;
+      // The running maximum moves only on jumps above 8; each lane tests its own scores, and the
+      // maximum over a column's rows is taken only when some lane finds a jump (as in prefill_item).
+      float alpha[NC];
+      bool jump = false;
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
-        const float mt = max_over_rows(fmax8(x[ct]));
-        // Key 0 is visible to every column; the running maximum moves only on jumps above 8.
-        const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
-        m_use[ct] = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
-        alpha[ct] = exp2_fast(m[ct] - m_use[ct]);
-        moved = moved || alpha[ct] != 1.0f;
+        alpha[ct] = 1.0f;
+        jump = jump || fmax8(x[ct]) * c > m[ct] + 8.0f;
       }
-      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+      if (__builtin_amdgcn_ballot_w64(jump) != 0) {
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
+          const float mt = max_over_rows(fmax8(x[ct]));
+          const float m_cand = __builtin_elementwise_maximum(m[ct], mt * c);
+          const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
+          alpha[ct] = exp2_fast(m[ct] - m_use);
+          m[ct] = m_use;
 #pragma unroll
           for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
           accl[ct] *= alpha[ct];
@@ -750,11 +749,10 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
       for (int ct = 0; ct < NC; ++ct) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m_use[ct]));
+        for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(x[ct][j], c, weight_log2_scale<DT>(8) - m[ct]));
         // fp16: the running sum is taken over the rounded weights, on the matrix cores (below)
         if constexpr (DT != kF16)
           l[ct] = fmaf(l[ct], alpha[ct], ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-        m[ct] = m_use[ct];
         u4 ph, pl;  // pl: bf16 remainder parts
         if constexpr (DT == kBF16) {
 #pragma unroll
