@@ -149,6 +149,27 @@ def test_launch_modes_agree_with_oracle(cuda, name, psize):
     assert np.abs(out - ref).max() <= TOL[x.cfg.dtype]
 
 
+@pytest.mark.parametrize("psize", [-2, 32])
+def test_more_pieces_per_wavefront_than_lds_row_slots(cuda, psize):
+    """A wavefront keeps the rows of at most 8 pieces in LDS until its last tile; further pieces
+    are written at once. 3000 one-tile contexts (and a few long ones, which are cut) over 8 kv
+    heads put about 12 whole segments in each balanced range, and with 32-token ranges a
+    wavefront loops over about 12 ranges: both paths run in one launch."""
+    import paged_attention_decode_amd as pa
+    lens = [16] * 3000
+    for i, L in ((7, 700), (1500, 1234), (2999, 333)):
+        lens[i] = L
+    x = make_inputs(custom_config(dtype="bf16", batch=len(lens), hq=16, hkv=8, d=128, lens=tuple(lens), seed=31))
+    plan = pa.decode_plan(len(lens), 16, 8, 128, 16, int(x.block_tables.shape[1]), pa.DTYPE_BF16,
+                          partition_size=psize)
+    assert plan["uses_reduce"]
+    _say(f"[gpu] LDS row slots overflow, partition_size={psize}, {plan['num_waves']} wavefronts")
+    dev = to_device(x, cuda)
+    out = _run_step(dev, x, partition_size=psize).cpu().numpy()
+    _, _, ref = oracle_after_store(x)
+    assert np.abs(out - ref).max() <= TOL["bf16"]
+
+
 CASES = [
     # dtype, batch, Hq, Hkv, D, bs, lengths
     ("bf16", 5, 8, 2, 128, 16, (1, 2, 15, 16, 17)),
