@@ -26,6 +26,8 @@ Prints ONE JSON line:
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample
                of the same workload (a reported baseline, not the target)
   workloads    (default run) the same record for each other workload
+  prefill      (default run) full-prompt paged prefill, TFLOP/s against the MFMA peak, on the
+               Llama-shaped (fp16) and skewed (bf16) workloads' prompts
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload NAME] [--prefill]
 """
@@ -52,6 +54,8 @@ RECORD_WORKLOADS = ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16", "long_ctx
 WORKLOAD_PARTITION = {"long_ctx_bf16": 512}
 # Workloads whose CPU baseline is also taken with one BLAS thread.
 ONE_THREAD_BASELINE = {"tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"}
+# Default run: full-prompt prefill records (TFLOP/s) of these workloads' prompts.
+PREFILL_RECORDS = ("llama32_1b_fp16", "skewed_prefix_bf16")
 KERNEL_SOURCE = ROOT / "paged_attention_decode_amd" / "csrc" / "decode.hip"
 PROFILES = ROOT / "profiles"
 COPY_BYTES = 256 << 20
@@ -651,6 +655,11 @@ def prefill_useful_flops(head_dim: int, num_heads: int, new_tokens, context_lens
 
 
 def prefill_bench(args) -> None:
+    """Full-prompt causal prefill over the workload's paged caches, as its own JSON line."""
+    print(json.dumps(measure_prefill(args.workload, args.steps, args.warmup)), flush=True)
+
+
+def measure_prefill(workload: str, steps: int, warmup: int) -> dict:
     """Full-prompt causal prefill over the workload's paged caches; useful flops = 4*D*Hq*sum(n*L - n(n-1)/2)."""
     import numpy as np
     import torch
@@ -659,7 +668,7 @@ def prefill_bench(args) -> None:
     from workloads import get_config, make_inputs, to_storage
 
     dev = torch.device("cuda:0")
-    cfg = get_config(args.workload)
+    cfg = get_config(workload)
     print(f"[bench] prefill: generating {cfg.name}", file=sys.stderr, flush=True)
     x = make_inputs(cfg)
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
@@ -680,30 +689,30 @@ def prefill_bench(args) -> None:
     qst = torch.from_numpy(qs).to(dev)
     out = torch.empty((int(qs[-1]), cfg.num_heads, cfg.head_dim), dtype=torch.float32, device=dev)
     flops = prefill_useful_flops(cfg.head_dim, cfg.num_heads, lens, lens)
-    for _ in range(max(1, args.warmup)):
+    for _ in range(max(1, warmup)):
         pa.paged_prefill(q, k_cache, v_cache, bt, cl, qst, x.scale, out)
     torch.cuda.synchronize()
     ev = [TimingEvent() for _ in range(2)]
     t0 = time.perf_counter()
     ev[0].record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         pa.paged_prefill(q, k_cache, v_cache, bt, cl, qst, x.scale, out)
     ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    ms = ev[0].elapsed_time(ev[1]) / steps
     tflops = flops / (ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[cfg.dtype]
-    print(json.dumps({
+    return {
         "metric": "paged prefill TFLOP/s (causal, full prompts)", "value": round(tflops, 2), "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3 / steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded, shapes of the workload)",
         "config": dict(describe(cfg), prompt_tokens=int(qs[-1]), useful_flops=flops),
         "tokens_per_s": round(float(qs[-1]) / (ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None, "kernel": "prefill_kernel",
-                     "kernel_mean_ms": round(ms, 5)}}), flush=True)
+                     "kernel_mean_ms": round(ms, 5)}}
 
 
 def _upload(a, dtype, dev):
@@ -1122,6 +1131,15 @@ def main():
         result["stream_read_ceiling"] = ceiling
     if records:
         result["workloads"] = records
+        # The next row's kernel (paged prefill), on the prompts of two workloads.
+        prefill = {}
+        for name in PREFILL_RECORDS:
+            print(f"[bench] prefill record {name}", file=sys.stderr, flush=True)
+            r = measure_prefill(name, 10, 2)
+            prefill[name] = {"value": r["value"], "unit": r["unit"], "dtype": r["dtype"],
+                             "ms_per_step": r["roofline"]["kernel_mean_ms"],
+                             "prompt_tokens": r["config"]["prompt_tokens"], "roofline": r["roofline"]}
+        result["prefill"] = prefill
     print(json.dumps(result), flush=True)
 
 
