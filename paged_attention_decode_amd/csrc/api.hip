@@ -563,6 +563,14 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
   }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Fused step where the attention kernel does not take the token itself: the token is written to
+  // its cache slot first, and the plain kernels run (neither writes the slot again).
+  if (a.k_new != nullptr && !decode_fuses_step(dtype, head_dim)) {
+    hipError_t err = launch_append(a, dtype, head_dim, s);
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "token append launch failed: %s", hipGetErrorString(err));
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+  }
   if (opts && opts->event_begin) {
     hipError_t err = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->event_begin), s);
     if (err != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord(begin) failed: %s", hipGetErrorString(err));

@@ -986,19 +986,47 @@ __global__ __launch_bounds__(256) void reduce_kernel(const DecodeArgs a) {
   }
 }
 
+// Fused decode step without the fused attention kernel: the step's token of every (sequence, kv
+// head) written to its cache slot (one wavefront each) before the plain kernels run.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void append_kernel(const DecodeArgs a) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (int64_t)a.num_seqs * a.num_kv_heads) return;
+  store_new_token<DT, D>(a, (int)(w / a.num_kv_heads), (int)(w % a.num_kv_heads), threadIdx.x & 63);
+}
+
+// Whether the attention kernel takes the step's token itself (fused decode step). At fp32 and
+// head_dim 256 the fused instance would hold the token's K/V rows (80 registers) beside the
+// tiles' and spill to scratch; there the token is written first (append_kernel).
+template <int DT, int D>
+constexpr bool kFusedStep = !(DT == kF32 && D == 256);
+
 template <int DT, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, int grid, size_t lds, hipStream_t st) {
   const dim3 g(grid), b(kDecodeThreads);
-  if (a.casc_width > 0) {
-    if (a.k_new != nullptr)
-      hipLaunchKernelGGL((decode_kernel<DT, D, true, true>), g, b, lds, st, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<DT, D, false, true>), g, b, lds, st, a);
-  } else if (a.k_new != nullptr) {
-    hipLaunchKernelGGL((decode_kernel<DT, D, true, false>), g, b, lds, st, a);
+  if constexpr (kFusedStep<DT, D>) {
+    if (a.k_new != nullptr) {
+      if (a.casc_width > 0)
+        hipLaunchKernelGGL((decode_kernel<DT, D, true, true>), g, b, lds, st, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<DT, D, true, false>), g, b, lds, st, a);
+      return hipGetLastError();
+    }
   } else {
-    hipLaunchKernelGGL((decode_kernel<DT, D, false, false>), g, b, lds, st, a);
+    if (a.k_new != nullptr) return hipErrorInvalidValue;  // the host writes the token first
   }
+  if (a.casc_width > 0)
+    hipLaunchKernelGGL((decode_kernel<DT, D, false, true>), g, b, lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT, D, false, false>), g, b, lds, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_append_t(const DecodeArgs& a, hipStream_t st) {
+  const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
+  if (waves == 0) return hipSuccess;
+  hipLaunchKernelGGL((append_kernel<DT, D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1048,6 +1076,39 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid,
 }
 
 hipError_t launch_share(const DecodeArgs& a, hipStream_t st) { return launch_share_t(a, st); }
+
+bool decode_fuses_step(int dtype, int head_dim) {
+  switch (dtype) {
+    case kF32:
+      return head_dim == 64 ? kFusedStep<kF32, 64> : head_dim == 128 ? kFusedStep<kF32, 128> : kFusedStep<kF32, 256>;
+    case kF16:
+      return head_dim == 64 ? kFusedStep<kF16, 64> : head_dim == 128 ? kFusedStep<kF16, 128> : kFusedStep<kF16, 256>;
+    default:
+      return head_dim == 64 ? kFusedStep<kBF16, 64> : head_dim == 128 ? kFusedStep<kBF16, 128>
+                                                                       : kFusedStep<kBF16, 256>;
+  }
+}
+
+hipError_t launch_append(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st) {
+  switch (dtype) {
+    case kF32:
+      if (head_dim == 64) return launch_append_t<kF32, 64>(a, st);
+      if (head_dim == 128) return launch_append_t<kF32, 128>(a, st);
+      if (head_dim == 256) return launch_append_t<kF32, 256>(a, st);
+      break;
+    case kF16:
+      if (head_dim == 64) return launch_append_t<kF16, 64>(a, st);
+      if (head_dim == 128) return launch_append_t<kF16, 128>(a, st);
+      if (head_dim == 256) return launch_append_t<kF16, 256>(a, st);
+      break;
+    case kBF16:
+      if (head_dim == 64) return launch_append_t<kBF16, 64>(a, st);
+      if (head_dim == 128) return launch_append_t<kBF16, 128>(a, st);
+      if (head_dim == 256) return launch_append_t<kBF16, 256>(a, st);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t st) {
   switch (dtype) {

@@ -145,6 +145,10 @@ hipError_t launch_prefill_shared(const PrefillArgs& a, int dtype, int head_dim, 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int grid, size_t lds_bytes,
                          hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// Fused decode step: whether the attention kernel takes the step's token itself; where it does
+// not, launch_append writes the token of every (sequence, kv head) to its cache slot first.
+bool decode_fuses_step(int dtype, int head_dim);
+hipError_t launch_append(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Shared-prefix detection: fills a.ws_share (one workgroup per window of a.casc_width sequences).
 hipError_t launch_share(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_store(const StoreArgs& a, int dtype, hipStream_t stream);
