@@ -217,7 +217,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   // Zero the values of keys at or beyond L (their slots may hold anything, and a zero weight
   // times a NaN is still NaN) and of a second tile that does not exist.
   auto mask_v = [&](int t0, bool has_b) {
-    if (t0 + 2 * kTile <= L && has_b) return;
+    // Only a sequence's last step reaches past L: a wave-uniform branch, kept as one (else the
+    // compiler turns it into selects and masks that every step would pay for).
+    const int full = __builtin_amdgcn_readfirstlane((t0 + 2 * kTile <= L && has_b) ? 1 : 0);
+    if (__builtin_expect(full != 0, 1)) return;
     uint32_t mk[2][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
