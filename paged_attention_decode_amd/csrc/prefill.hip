@@ -525,10 +525,11 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
 //   [0, T)     K tile A: chunk j of lane (kq, ln) = key chunk 4j + kq of token ln, which is
 //              exactly the first product's operand, read back by the same lane
 //   [T, 2T)    K tile B
-//   [2T, 3T)   V tile A: chunk j of lane (kq, ln) = keys 4kq .. 4kq+3 of dims 32j + 2ln, +1
-//   [3T, 4T)   V tile B
-// The second product's operand for dim 32w + e (e < 32) and lane group kq is 8 bytes of each V
-// tile, at chunk (w, kq, e / 2), half e % 2; lanes ln = 0..15 read 128 contiguous bytes.
+//   [2T, 4T)   V of both tiles: 16 bytes per (dim 32w + e, key group kq), at ((w * 4 + kq) * 32
+//              + e) * 16: keys 4kq .. 4kq+3 of tile A, then of tile B. That is exactly the second
+//              product's operand for dim 32w + e and lane group kq, one 16-byte read; lanes
+//              ln = 0..15 read 256 contiguous bytes. Each V loader lane stores its chunk's two dims
+//              (2ln, 2ln + 1) as two 8-byte halves.
 template <int DT, int D>
 struct SharedCfg {
   using C = Cfg<DT, D>;
@@ -651,9 +652,21 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
         for (int j = 0; j < C::kLoads; ++j) stg[j] &= u4{m01, m23, m01, m23};
       }
     }
-    char* dst = buf + wv * T + lane * 16;
+    if (share_k) {
+      char* dst = buf + wv * T + lane * 16;
 #pragma unroll
-    for (int j = 0; j < C::kLoads; ++j) *reinterpret_cast<u4*>(dst + j * 1024) = stg[j];
+      for (int j = 0; j < C::kLoads; ++j) *reinterpret_cast<u4*>(dst + j * 1024) = stg[j];
+    } else {
+      // V: the chunk's two dims (2ln, 2ln + 1), 8 bytes each, go to their (dim, key group) slots,
+      // beside the other tile's 8 bytes of the same dim and keys.
+      char* dst = buf + 2 * T + half * 8;
+#pragma unroll
+      for (int j = 0; j < C::kLoads; ++j) {
+        const int slot = (j * 4 + kq) * 32 + 2 * ln;
+        *reinterpret_cast<u2*>(dst + slot * 16) = u2{stg[j].x, stg[j].y};
+        *reinterpret_cast<u2*>(dst + (slot + 1) * 16) = u2{stg[j].z, stg[j].w};
+      }
+    }
   };
 
 
@@ -696,16 +709,14 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
           }
         }
       }
-      // V^T operands: dims 32w + ln (va0) and 32w + 16 + ln (va1), keys of tile A then tile B.
+      // V^T operands: dims 32w + ln (va0) and 32w + 16 + ln (va1), keys of tile A then tile B: one
+      // 16-byte read each, already in operand order.
       u4 va0[C::kLoads], va1[C::kLoads];
-      const int vo = (kq * 16 + (ln >> 1)) * 16 + (ln & 1) * 8;
 #pragma unroll
       for (int w = 0; w < C::kLoads; ++w) {
-        const char* va = buf + 2 * T + w * 1024 + vo;
-        const u2 a0 = *reinterpret_cast<const u2*>(va), b0 = *reinterpret_cast<const u2*>(va + T);
-        const u2 a1 = *reinterpret_cast<const u2*>(va + 128), b1 = *reinterpret_cast<const u2*>(va + T + 128);
-        va0[w] = u4{a0[0], a0[1], b0[0], b0[1]};
-        va1[w] = u4{a1[0], a1[1], b1[0], b1[1]};
+        const char* va = buf + 2 * T + ((w * 4 + kq) * 32 + ln) * 16;
+        va0[w] = *reinterpret_cast<const u4*>(va);
+        va1[w] = *reinterpret_cast<const u4*>(va + 256);
       }
       const bool open = t0 + 2 * kTile - 1 <= p_first;
       // One causal-mask branch and one rescale branch for all column tiles, as in prefill_item.
