@@ -525,11 +525,12 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
 //   [0, T)     K tile A: chunk j of lane (kq, ln) = key chunk 4j + kq of token ln, which is
 //              exactly the first product's operand, read back by the same lane
 //   [T, 2T)    K tile B
-//   [2T, 4T)   V of both tiles: 16 bytes per (dim 32w + e, key group kq), at ((w * 4 + kq) * 32
-//              + e) * 16: keys 4kq .. 4kq+3 of tile A, then of tile B. That is exactly the second
-//              product's operand for dim 32w + e and lane group kq, one 16-byte read; lanes
-//              ln = 0..15 read 256 contiguous bytes. Each V loader lane stores its chunk's two dims
-//              (2ln, 2ln + 1) as two 8-byte halves.
+//   [2T, 4T)   V of both tiles: the 8 bytes of keys 4kq .. 4kq+3 of dim 32w + e of tile h at
+//              (w * 4 + kq) * 512 + (e / 16) * 256 + h * 128 + (e % 16) * 8. A V loader lane's
+//              chunk (dims 2ln, 2ln + 1 of one tile) is 16 contiguous bytes there, and eight lanes
+//              fill 128 contiguous bytes (no bank conflicts). The second product's operand for dim
+//              32w + e and lane group kq is tile A's 8 bytes and tile B's, 128 bytes apart: one
+//              paired read, in operand order; lanes ln = 0..15 read 128 contiguous bytes each.
 template <int DT, int D>
 struct SharedCfg {
   using C = Cfg<DT, D>;
@@ -537,6 +538,9 @@ struct SharedCfg {
   static constexpr int kTileBytes = kTile * D * C::kE;
   static constexpr int kBufBytes = 4 * kTileBytes;
 };
+
+// Offset of key group kq's block in the V layout of one step (chunk / dim group 0).
+__device__ __forceinline__ int j0_kq_base(int kq) { return kq * 512; }
 
 template <int DT, int D>
 __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s, int g, int hg, int qbg, int wv,
@@ -643,7 +647,9 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
   auto store_share = [&](int st, char* buf) {
     if (!share_k) {
       const int t0 = share_tile(st) * kTile;
-      if (t0 + kTile > L) {
+      // Only a sequence's last tile reaches past L: kept a real, wave-uniform branch.
+      const int past = __builtin_amdgcn_readfirstlane(t0 + kTile > L ? 1 : 0);
+      if (__builtin_expect(past != 0, 0)) {
         const bool v0 = t0 + 4 * kq + 0 < L, v1 = t0 + 4 * kq + 1 < L;
         const bool v2 = t0 + 4 * kq + 2 < L, v3 = t0 + 4 * kq + 3 < L;
         const uint32_t m01 = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
@@ -657,15 +663,11 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
 #pragma unroll
       for (int j = 0; j < C::kLoads; ++j) *reinterpret_cast<u4*>(dst + j * 1024) = stg[j];
     } else {
-      // V: the chunk's two dims (2ln, 2ln + 1), 8 bytes each, go to their (dim, key group) slots,
-      // beside the other tile's 8 bytes of the same dim and keys.
-      char* dst = buf + 2 * T + half * 8;
+      // V: the chunk (dims 32j + 2ln, +1 of key group kq) is 16 contiguous bytes of the layout
+      // below; eight lanes fill 128 contiguous bytes.
+      char* dst = buf + 2 * T + (j0_kq_base(kq) + (ln >> 3) * 256 + half * 128 + (ln & 7) * 16);
 #pragma unroll
-      for (int j = 0; j < C::kLoads; ++j) {
-        const int slot = (j * 4 + kq) * 32 + 2 * ln;
-        *reinterpret_cast<u2*>(dst + slot * 16) = u2{stg[j].x, stg[j].y};
-        *reinterpret_cast<u2*>(dst + (slot + 1) * 16) = u2{stg[j].z, stg[j].w};
-      }
+      for (int j = 0; j < C::kLoads; ++j) *reinterpret_cast<u4*>(dst + j * 2048) = stg[j];
     }
   };
 
@@ -709,14 +711,16 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
           }
         }
       }
-      // V^T operands: dims 32w + ln (va0) and 32w + 16 + ln (va1), keys of tile A then tile B: one
-      // 16-byte read each, already in operand order.
+      // V^T operands: dims 32w + ln (va0) and 32w + 16 + ln (va1), keys of tile A then tile B:
+      // each two 8-byte reads 128 bytes apart (one paired LDS read), in operand order.
       u4 va0[C::kLoads], va1[C::kLoads];
 #pragma unroll
       for (int w = 0; w < C::kLoads; ++w) {
-        const char* va = buf + 2 * T + ((w * 4 + kq) * 32 + ln) * 16;
-        va0[w] = *reinterpret_cast<const u4*>(va);
-        va1[w] = *reinterpret_cast<const u4*>(va + 256);
+        const char* va = buf + 2 * T + w * 2048 + j0_kq_base(kq) + ln * 8;
+        const u2 a0 = *reinterpret_cast<const u2*>(va), b0 = *reinterpret_cast<const u2*>(va + 128);
+        const u2 a1 = *reinterpret_cast<const u2*>(va + 256), b1 = *reinterpret_cast<const u2*>(va + 384);
+        va0[w] = u4{a0[0], a0[1], b0[0], b0[1]};
+        va1[w] = u4{a1[0], a1[1], b1[0], b1[1]};
       }
       const bool open = t0 + 2 * kTile - 1 <= p_first;
       // One causal-mask branch and one rescale branch for all column tiles, as in prefill_item.
