@@ -477,13 +477,21 @@ def describe(cfg) -> dict:
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it, with its family and model numbers (virtual machines
+    often report a generic name) and the logical CPUs the system has."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "vendor_id") and k not in fields:
+                    fields[k] = v
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    extra = [f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model") if k in fields]
+    extra.append(f"{os.cpu_count()} logical CPUs")
+    return f"{name} ({', '.join(extra)})"
 
 
 def cpu_baseline(x, gpu_out, budget_s: float, one_thread_budget_s: float = 0.0) -> dict:
