@@ -22,7 +22,7 @@ Prints ONE JSON line:
                current kernel source
   cold_step, split_cold_median_us   cold step time and its store / attention /
                merge-and-gaps split
-  stream_read_ceiling  best rate of a plain streaming-read kernel on the box
+  stream_read_ceiling  best rate of a plain streaming-read kernel on this GPU
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample
                of the same workload (a reported baseline, not the target)
   workloads    (default run) the same record for each other workload
@@ -258,7 +258,7 @@ def summarize_sq(workload: str, directories, commands, kernel: str = "decode") -
     Shares of SQ_WAVE_CYCLES are per wavefront: how much of its life a wavefront spent issuing
     VALU, waiting for an instruction to issue, or waiting on s_waitcnt / a barrier. The MFMA pipe
     busy fraction compares SQ_VALU_MFMA_BUSY_CYCLES with the kernel's SIMD-cycles, taken from the
-    run's timestamps at the box's 2.4 GHz peak clock, so it is a lower bound."""
+    run's timestamps at the GPU's 2.4 GHz peak clock, so it is a lower bound."""
     import csv
     name = "prefill" if kernel == "prefill" else "decode_kernel"
     tot, disp, span = {}, {}, {}

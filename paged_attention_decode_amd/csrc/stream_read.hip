@@ -8,7 +8,7 @@
 // The loaded words are summed into one 32-bit word per lane and written to `sink`, so no
 // load is dead; the sink is 256 bytes per wavefront, negligible next to the buffer.
 //
-// The rate this kernel reaches is the practical HBM read ceiling of the box for this access
+// The rate this kernel reaches is the practical HBM read ceiling of the GPU for this access
 // pattern: the decode kernel's K/V bandwidth is reported as a fraction of it as well as of the
 // 8 TB/s peak.
 
