@@ -26,7 +26,9 @@ Prints ONE JSON line:
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample
                of the same workload (a reported baseline, not the target)
   workloads    (default run) the same record for each other workload
-  prefill      (default run) full-prompt paged prefill, TFLOP/s against the MFMA peak, on the
+  prefill      (default run) full-prompt paged prefill, TFLOP/s against the MFMA peak and
+               against the measured matrix-core ceiling (a loop of independent 16x16x32
+               instructions of the prompt's dtype, two wavefronts per SIMD), on the
                Llama-shaped (fp16) and skewed (bf16) workloads' prompts
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload NAME] [--prefill]
@@ -667,6 +669,56 @@ def prefill_bench(args) -> None:
     print(json.dumps(measure_prefill(args.workload, args.steps, args.warmup)), flush=True)
 
 
+class MfmaCeiling:
+    """The matrix-core loop of libpa_stream_read.so (measurement only): eight independent chains of
+    one matrix-core instruction kind per wavefront, nothing else, two workgroups of four
+    wavefronts on every compute unit (two wavefronts per SIMD, as the prefill kernels run)."""
+
+    KINDS = {"bf16": (0, "v_mfma_f32_16x16x32_bf16", 16384), "fp16": (1, "v_mfma_f32_16x16x32_f16", 16384),
+             "bf16_16x16x16": (2, "v_mfma_f32_16x16x16_bf16", 8192)}
+
+    def __init__(self, dev):
+        import ctypes
+        import torch
+        lib_path = ROOT / "paged_attention_decode_amd" / "libpa_stream_read.so"
+        if not lib_path.exists():
+            raise RuntimeError(f"{lib_path} is not built: run `python -m paged_attention_decode_amd.build`")
+        self.lib = ctypes.CDLL(str(lib_path))
+        self.lib.pa_bench_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.pa_bench_mfma.restype = ctypes.c_int
+        self.cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        self.dev = dev
+
+    def measure(self, kind: str, iters: int = 16000, reps: int = 5) -> dict:
+        """Best rate over `reps` launches of 2 * cus workgroups, each asking for 64 KiB of LDS so
+        that a compute unit holds exactly two."""
+        import torch
+        k, name, flops_each = self.KINDS[kind]
+        grid = self.cus * 2
+        sink = torch.empty(grid * 256, dtype=torch.float32, device=self.dev)
+        stream = torch.cuda.current_stream(self.dev).cuda_stream
+
+        def launch():
+            if self.lib.pa_bench_mfma(k, iters, grid, 65536, sink.data_ptr(), stream) != 0:
+                raise RuntimeError("pa_bench_mfma failed")
+
+        launch()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        flops = float(grid) * 4 * 8 * iters * flops_each
+        return {"instruction": name, "waves_per_simd": 2, "tflops": round(flops / (best * 1e-3) / 1e12, 1),
+                "ms": round(best, 4), "what": f"best of {reps} launches of the matrix-core loop"}
+
+
 def measure_prefill(workload: str, steps: int, warmup: int) -> dict:
     """Full-prompt causal prefill over the workload's paged caches; useful flops = 4*D*Hq*sum(n*L - n(n-1)/2)."""
     import numpy as np
@@ -711,6 +763,10 @@ def measure_prefill(workload: str, steps: int, warmup: int) -> dict:
     ms = ev[0].elapsed_time(ev[1]) / steps
     tflops = flops / (ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    ceiling = None
+    if cfg.dtype in MfmaCeiling.KINDS:
+        ceiling = MfmaCeiling(dev).measure(cfg.dtype)
+        ceiling["prefill_frac_of_ceiling"] = round(tflops / ceiling["tflops"], 4)
     return {
         "metric": "paged prefill TFLOP/s (causal, full prompts)", "value": round(tflops, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(wall * 1e3 / steps, 4),
@@ -720,7 +776,7 @@ def measure_prefill(workload: str, steps: int, warmup: int) -> dict:
         "tokens_per_s": round(float(qs[-1]) / (ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None, "kernel": "prefill_kernel",
-                     "kernel_mean_ms": round(ms, 5)}}
+                     "kernel_mean_ms": round(ms, 5), "mfma_ceiling": ceiling}}
 
 
 def _upload(a, dtype, dev):

@@ -1,16 +1,25 @@
-// Streaming-read ceiling for the decode benchmark (measurement only; built as its own library,
-// libpa_stream_read.so, and not part of libpagedattn's ABI).
+// Practical ceilings for the benchmark (measurement only; built as its own library,
+// libpa_stream_read.so, and not part of libpagedattn's ABI): a streaming read for the decode
+// kernel's HBM bound and a matrix-core loop for the prefill kernel's MFMA bound.
 //
-// Reads a large device buffer once with the loads the decode kernel uses for K/V pages: 16-byte
-// buffer loads, every lane of a wavefront on consecutive 16-byte chunks (1 KiB per load
-// instruction), with the default or the non-temporal cache policy. Each wavefront keeps UNROLL
-// such loads in flight per round and walks the buffer with a stride of all wavefronts' rounds.
-// The loaded words are summed into one 32-bit word per lane and written to `sink`, so no
+// Streaming read. Reads a large device buffer once with the loads the decode kernel uses for K/V
+// pages: 16-byte buffer loads, every lane of a wavefront on consecutive 16-byte chunks (1 KiB per
+// load instruction), with the default or the non-temporal cache policy. Each wavefront keeps
+// UNROLL such loads in flight per round and walks the buffer with a stride of all wavefronts'
+// rounds. The loaded words are summed into one 32-bit word per lane and written to `sink`, so no
 // load is dead; the sink is 256 bytes per wavefront, negligible next to the buffer.
 //
 // The rate this kernel reaches is the practical HBM read ceiling of the GPU for this access
 // pattern: the decode kernel's K/V bandwidth is reported as a fraction of it as well as of the
 // 8 TB/s peak.
+//
+// Matrix-core loop. Every wavefront issues `iters` rounds of eight independent matrix-core
+// instructions of one kind (the prefill kernel's 16x16x32 bf16 / fp16 forms, or the decode
+// kernel's 16x16x16 bf16 form) on register operands, eight accumulator chains so that no
+// instruction waits for the previous one's result. Nothing else runs, so the rate it reaches, at
+// whatever clock the GPU holds under that load, is the practical matrix-core ceiling. The caller
+// may ask for unused LDS per workgroup, which caps how many workgroups share a compute unit and so
+// spreads the grid evenly over the compute units.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,6 +85,45 @@ hipError_t launch_pol(int unroll, const void* buf, uint32_t bytes, int grid, uin
   return hipGetLastError();
 }
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 h8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef short s4 __attribute__((__vector_size__(4 * sizeof(short))));
+
+template <int KIND>
+__device__ __forceinline__ f4 mfma(u4 a, u4 b, f4 c) {
+  if constexpr (KIND == 0) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+  } else if constexpr (KIND == 1) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+  } else {
+    const s4 a2 = __builtin_bit_cast(s4, __builtin_shufflevector(a, a, 0, 1));
+    const s4 b2 = __builtin_bit_cast(s4, __builtin_shufflevector(b, b, 0, 1));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a2, b2, c, 0, 0, 0);
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void mfma_loop_kernel(int iters, uint32_t seed, float* sink) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  // Small finite operands that depend on the lane and on a kernel argument, so nothing folds.
+  const uint32_t w = ((seed + (uint32_t)lane) & 0x7Fu) | 0x3C00u;  // fp16 / bf16 bits in [1, 2)
+  const u4 a = u4{w | (w << 16), w | (w << 16), w | (w << 16), w | (w << 16)};
+  const u4 b = u4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u} ^ u4{seed & 1u, 0u, 0u, 0u};
+  f4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = mfma<KIND>(a, b, acc[i]);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  sink[(uint64_t)wave * 64 + lane] = sum;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,6 +146,29 @@ int pa_bench_stream_read(const void* buf, uint64_t bytes, int policy, int unroll
   const hipError_t e = policy == 0 ? launch_pol<0>(unroll, buf, (uint32_t)bytes, grid, out, s)
                                    : launch_pol<2>(unroll, buf, (uint32_t)bytes, grid, out, s);
   return e == hipSuccess ? 0 : 2;
+}
+
+/*
+ * pa_bench_mfma - matrix-core loop: every wavefront of `grid` workgroups (256 threads, 4
+ * wavefronts) issues iters * 8 instructions of one kind:
+ *   kind 0  v_mfma_f32_16x16x32_bf16   (16384 flops each)
+ *   kind 1  v_mfma_f32_16x16x32_f16    (16384 flops each)
+ *   kind 2  v_mfma_f32_16x16x16_bf16   (8192 flops each)
+ *   lds_bytes  unused LDS requested per workgroup (at most 65536), to cap the workgroups a
+ *           compute unit holds: 65536 allows two of them on gfx950's 160 KiB.
+ *   sink    device memory of grid * 256 * 4 bytes, written (contents meaningless).
+ * Returns 0, or a nonzero code for bad arguments (nothing launched) or a launch error.
+ */
+int pa_bench_mfma(int kind, int iters, int grid, int lds_bytes, void* sink, void* stream) {
+  if (!sink || grid <= 0 || iters <= 0 || kind < 0 || kind > 2 || lds_bytes < 0 || lds_bytes > 65536) return 1;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* out = static_cast<float*>(sink);
+  const uint32_t seed = 0x35u;
+  const size_t lds = (size_t)lds_bytes;
+  if (kind == 0) hipLaunchKernelGGL((mfma_loop_kernel<0>), dim3(grid), dim3(kThreads), lds, s, iters, seed, out);
+  if (kind == 1) hipLaunchKernelGGL((mfma_loop_kernel<1>), dim3(grid), dim3(kThreads), lds, s, iters, seed, out);
+  if (kind == 2) hipLaunchKernelGGL((mfma_loop_kernel<2>), dim3(grid), dim3(kThreads), lds, s, iters, seed, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 }  // extern "C"

@@ -113,3 +113,27 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_measurement_library_rejects_bad_arguments_before_any_launch():
+    """libpa_stream_read.so (the streaming-read and matrix-core ceilings) exports both entry points
+    and checks its arguments on the host: each bad call returns 1 without touching the GPU."""
+    import ctypes
+    lib_path = ROOT / "paged_attention_decode_amd" / "libpa_stream_read.so"
+    if not lib_path.exists():
+        pytest.skip("measurement library not built")
+    lib = ctypes.CDLL(str(lib_path))
+    lib.pa_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_bench_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
+    assert lib.pa_bench_stream_read(None, 1 << 20, 0, 8, 4, p, None) == 1
+    assert lib.pa_bench_stream_read(p, 1000, 0, 8, 4, p, None) == 1          # not a multiple of 16 KiB
+    assert lib.pa_bench_stream_read(p, 1 << 31, 0, 8, 4, p, None) == 1       # past one buffer resource
+    assert lib.pa_bench_stream_read(p, 1 << 20, 3, 8, 4, p, None) == 1       # unknown policy
+    assert lib.pa_bench_mfma(3, 10, 4, 0, p, None) == 1                      # unknown kind
+    assert lib.pa_bench_mfma(0, 0, 4, 0, p, None) == 1                       # no iterations
+    assert lib.pa_bench_mfma(0, 10, 0, 0, p, None) == 1                      # empty grid
+    assert lib.pa_bench_mfma(0, 10, 4, 65537, p, None) == 1                  # LDS request too large
+    assert lib.pa_bench_mfma(0, 10, 4, 0, None, None) == 1                   # no sink
