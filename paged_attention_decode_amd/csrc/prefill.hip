@@ -322,7 +322,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     for (int ct = 0; ct < NC; ++ct) {
       alpha[ct] = 1.0f;
       // IEEE-2019 maximum: gfx950 has a three-input form, and it needs no NaN quieting first.
-      jump = jump || fmax8(x[ct]) * c > m[ct] + 8.0f;
+      // Bitwise or: a short-circuit || would become a masked branch per column tile.
+      jump = jump | (fmax8(x[ct]) * c > m[ct] + 8.0f);
     }
     if (__builtin_amdgcn_ballot_w64(jump) != 0) {
 #pragma unroll
@@ -748,7 +749,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
         alpha[ct] = 1.0f;
-        jump = jump || fmax8(x[ct]) * c > m[ct] + 8.0f;
+        jump = jump | (fmax8(x[ct]) * c > m[ct] + 8.0f);
       }
       if (__builtin_amdgcn_ballot_w64(jump) != 0) {
 #pragma unroll
