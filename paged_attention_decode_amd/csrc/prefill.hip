@@ -130,9 +130,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   f4 acc[NC][C::kAcc];
   f4 accl[NC];  // fp16: running sums of the rounded weights (matrix cores; every row the same)
   float m[NC], l[NC];
+  float thr[NC];  // (m + 8) / c: a raw score above it moves the running maximum
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
     m[ct] = -INFINITY;
+    thr[ct] = -INFINITY;
     l[ct] = 0.f;
 #pragma unroll
     for (int u = 0; u < C::kAcc; ++u) acc[ct][u] = f4{0.f, 0.f, 0.f, 0.f};
@@ -150,7 +152,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * page_bytes;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * page_bytes;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
-  const int64_t nb_max = a.num_blocks - 1;
+  // Block ids are int32: clamped in 32 bits, into [0, num_blocks - 1].
+  const int nb_max = (int)(a.num_blocks - 1 < INT32_MAX ? a.num_blocks - 1 : INT32_MAX);
   // Lane offsets inside a page. K: chunk (4j + kq) of token (off0 + ln). V, 16-bit: 8 bytes =
   // tokens off0 + 4kq .. +3 of dim 32w + ln (and of dim 32w + 16 + ln at +128 bytes). V, fp32:
   // 16 bytes = tokens off0 + 4kq .. +3 of dim 16u + ln.
@@ -172,8 +175,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     return make_int2(cbt[(tile_of(sc, 0) * kTile) >> a.bs_log2], cbt[(tile_of(sc, 1) * kTile) >> a.bs_log2]);
   };
   auto block = [&](int raw) -> int64_t {
-    const int64_t b = __builtin_amdgcn_readfirstlane(raw);
-    return b < 0 ? 0 : (b > nb_max ? nb_max : b);
+    const int b = __builtin_amdgcn_readfirstlane(raw);
+    return (int64_t)min(max(b, 0), nb_max);
   };
   u4 kA[C::kLoads], kB[C::kLoads];
   // 16-bit: vr0[w] / vr1[w] are the second product's V^T operands for dims 32w + ln /
@@ -311,19 +314,24 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
     }
     // The running maximum m of each column is kept unless a score exceeds it by more than 8
     // (log2 units): weights stay below 2^8, and the accumulators are rescaled only on such
-    // jumps. Each lane tests its own scores against m + 8 (c > 0, and rounding keeps the order,
-    // so a lane's maximum times c exceeds m + 8 exactly when the column's does); only when some
-    // lane finds a jump is the maximum over the column's rows taken. That happens on an item's
-    // first step (m = -inf; key 0 is visible to every column, so m is finite afterwards) and on
-    // real jumps. Columns without a jump keep alpha = 1.
+    // jumps. Each lane tests its own raw scores against thr = (m + 8) / c (c > 0), kept with m,
+    // so the test costs no arithmetic per score; only when some lane finds a jump is the
+    // maximum over the column's rows taken. That happens on an item's first step (m = -inf; key
+    // 0 is visible to every column, so m is finite afterwards) and on real jumps. Columns
+    // without a jump keep alpha = 1. Where x > thr and x * c > m + 8 disagree (within a rounding
+    // of the threshold) either no rescale happens and a weight exceeds 2^8 by a rounding, or
+    // the rescale finds m + 8 not exceeded and keeps m: both harmless.
     float alpha[NC];
     bool jump = false;
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
       alpha[ct] = 1.0f;
       // IEEE-2019 maximum: gfx950 has a three-input form, and it needs no NaN quieting first.
-      // Bitwise or: a short-circuit || would become a masked branch per column tile.
-      jump = jump | (fmax8(x[ct]) * c > m[ct] + 8.0f);
+      // Bitwise or: a short-circuit || would become a masked branch per column tile. The bf16
+      // head_dim-64 instance keeps ||: straight-line, its registers overflow into AGPRs and it
+      // drops to one wavefront per SIMD.
+      if constexpr (DT == kBF16 && D == 64) jump = jump || fmax8(x[ct]) > thr[ct];
+      else jump = jump | (fmax8(x[ct]) > thr[ct]);
     }
     if (__builtin_amdgcn_ballot_w64(jump) != 0) {
 #pragma unroll
@@ -333,6 +341,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
         const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
         alpha[ct] = exp2_fast(m[ct] - m_use);
         m[ct] = m_use;
+        thr[ct] = (m_use + 8.0f) / c;
 #pragma unroll
         for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
         accl[ct] *= alpha[ct];
@@ -596,9 +605,11 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
   f4 acc[NC][C::kAcc];
   f4 accl[NC];  // fp16: running sums of the rounded weights (matrix cores; every row the same)
   float m[NC], l[NC];
+  float thr[NC];  // (m + 8) / c: a raw score above it moves the running maximum
 #pragma unroll
   for (int ct = 0; ct < NC; ++ct) {
     m[ct] = -INFINITY;
+    thr[ct] = -INFINITY;
     l[ct] = 0.f;
 #pragma unroll
     for (int u = 0; u < C::kAcc; ++u) acc[ct][u] = f4{0.f, 0.f, 0.f, 0.f};
@@ -613,7 +624,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
   const int64_t page_bytes = (int64_t)bs * D * C::kE;
   const int page_bytes32 = (int)page_bytes;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * page_bytes;
-  const int64_t nb_max = a.num_blocks - 1;
+  const int nb_max = (int)(a.num_blocks - 1 < INT32_MAX ? a.num_blocks - 1 : INT32_MAX);
   const int tiles = p_last_wg / kTile + 1;
   const int steps = (tiles + 1) >> 1;
   const_i32* cbt = (const_i32*)(a.block_tables + (int64_t)s * a.max_blocks);
@@ -632,8 +643,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
   u4 stg[C::kLoads];
   auto load_share = [&](int st, int raw) {
     const int tile = share_tile(st);
-    int64_t blk = __builtin_amdgcn_readfirstlane(raw);
-    blk = blk < 0 ? 0 : (blk > nb_max ? nb_max : blk);
+    const int64_t blk = min(max((int)__builtin_amdgcn_readfirstlane(raw), 0), nb_max);
     // A tile that does not exist (an odd last step) loads zeros and reads no memory.
     const int bytes = 2 * st + half < tiles ? page_bytes32 : 0;
     const __amdgpu_buffer_rsrc_t r = page_rsrc(sbase + blk * blk_stride, bytes);
@@ -749,7 +759,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
 #pragma unroll
       for (int ct = 0; ct < NC; ++ct) {
         alpha[ct] = 1.0f;
-        jump = jump | (fmax8(x[ct]) * c > m[ct] + 8.0f);
+        jump = jump | (fmax8(x[ct]) > thr[ct]);
       }
       if (__builtin_amdgcn_ballot_w64(jump) != 0) {
 #pragma unroll
@@ -759,6 +769,7 @@ __device__ __forceinline__ void prefill_shared_item(const PrefillArgs& a, int s,
           const float m_use = m_cand > m[ct] + 8.0f ? m_cand : m[ct];
           alpha[ct] = exp2_fast(m[ct] - m_use);
           m[ct] = m_use;
+          thr[ct] = (m_use + 8.0f) / c;
 #pragma unroll
           for (int u = 0; u < C::kAcc; ++u) acc[ct][u] *= alpha[ct];
           accl[ct] *= alpha[ct];
