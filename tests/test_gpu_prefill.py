@@ -111,6 +111,40 @@ def test_bf16_prefill_with_large_values(cuda, d):
     assert np.abs(ref).max() > 100.0  # the large values do reach the output
 
 
+@pytest.mark.parametrize("dt,d", [("fp16", 64), ("bf16", 128), ("bf16", 64)])
+def test_prefill_with_large_logits(cuda, dt, d):
+    """Logits in the thousands (log2 units): q and K scaled by 32 (exact, a power of two), so the
+    running maximum jumps by hundreds from key to key and most rescales flush the accumulators.
+    Covers the per-wavefront kernel (fp16 and bf16 at head_dim 64) and the workgroup-shared one
+    (bf16 at 128) against the oracle, inside the score range the lazy rescale assumes."""
+    import torch
+    import paged_attention_decode_amd as pa
+    from _paged_helpers import widen_np
+    hq, hkv = 8, 2
+    lens, news = (260, 97, 33), (260, 40, 33)
+    x = make_inputs(custom_config(dtype=dt, batch=3, hq=hq, hkv=hkv, d=d, lens=lens, seed=505))
+    x.k_cache = to_storage((widen_np(x.k_cache, dt) * 32.0).astype(np.float32), dt)
+    rng = np.random.default_rng(505)
+    qs = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = to_storage(32.0 * rng.standard_normal((int(qs[-1]), hq, d), dtype=np.float32), dt)
+    dev = to_device(x, cuda)
+    out = pa.paged_prefill(np_to_torch(q, dt).to(cuda), dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                           dev["context_lens"], torch.from_numpy(qs).to(cuda), x.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref = oracle.prefill(q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, qs, x.scale, geometry(x))
+    err = np.abs(out - ref)
+    # The logits' spread, in log2 units: the scores the kernel's running maximum tracks.
+    geo = geometry(x)
+    kk, _ = oracle.gather_kv(x.k_cache, x.v_cache, x.block_tables[0], int(lens[0]), geo)
+    spread = np.abs(widen_np(q[:news[0]], dt)[:, 0] @ kk[:, 0].T).max() * x.scale / np.log(2.0)
+    print(f"[gpu] large logits {dt} head_dim {d}: max |logit| {spread:.0f} (log2), max err {err.max():.2e}",
+          flush=True)
+    assert spread > 1000.0
+    assert np.isfinite(out[: int(qs[-1])]).all()
+    assert (err <= TOL[dt]).all(), err.max()
+
+
 def test_store_then_prefill_then_decode_chain(cuda):
     """A prompt stored and prefilled, then one decode step: both against the oracle."""
     import torch
