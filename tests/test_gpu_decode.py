@@ -149,6 +149,25 @@ def test_launch_modes_agree_with_oracle(cuda, name, psize):
     assert np.abs(out - ref).max() <= TOL[x.cfg.dtype]
 
 
+@pytest.mark.parametrize("psize", [-3, -2, -1, 32])
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("fp16", 64)])
+def test_large_logits_in_every_mode(cuda, dt, d, psize):
+    """q and K scaled by 32 (exact, a power of two): logits in the thousands (log2 units), so each
+    tile moves the running maximum by hundreds, and split pieces of one context carry log-sum-exp
+    values far apart (most merge weights underflow to zero). Store + decode against the oracle."""
+    from _paged_helpers import widen_np
+    _say(f"[gpu] large logits {dt} head_dim {d} partition_size={psize}")
+    x = make_inputs(custom_config(dtype=dt, batch=5, hq=8, hkv=2, d=d, lens=(1, 40, 300, 777, 1500), seed=606))
+    x.k_cache = to_storage((widen_np(x.k_cache, dt) * 32.0).astype(np.float32), dt)
+    x.k_new = to_storage((widen_np(x.k_new, dt) * 32.0).astype(np.float32), dt)
+    x.q = to_storage((widen_np(x.q, dt) * 32.0).astype(np.float32), dt)
+    dev = to_device(x, cuda)
+    out = _run_step(dev, x, partition_size=psize).cpu().numpy()
+    _, _, ref = oracle_after_store(x)
+    assert np.isfinite(out).all()
+    assert np.abs(out - ref).max() <= TOL[dt], np.abs(out - ref).max()
+
+
 @pytest.mark.parametrize("psize", [-2, 32])
 def test_more_pieces_per_wavefront_than_lds_row_slots(cuda, psize):
     """A wavefront keeps the rows of at most 8 pieces in LDS until its last tile; further pieces
