@@ -324,6 +324,11 @@ int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t 
  *                rows but never a q read or out write outside the buffers.
  *   out          [num_tokens][num_heads][head_dim] contiguous, fp32 or dtype.
  *   Other arguments and limits as for pa_paged_attention_decode.
+ * Workgroups take their work items from counters in a small fixed array of the library (no
+ * allocation; every launch leaves its counters at zero when it ends, so calls can be recorded
+ * into a HIP graph). Calls take the 64 sets of counters in turn: calls that run at the same time
+ * on one device (other streams, or replays of captured calls) must not number 64 or more, or two
+ * of them may share counters and skip work.
  */
 int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,

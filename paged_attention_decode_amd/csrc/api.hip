@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <climits>
 #include <mutex>
 #include <string>
@@ -367,6 +368,10 @@ int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache,
   a.bs_log2 = ilog2(block_size);
   a.max_blocks = max_blocks_per_seq;
   a.out_f32 = out_dtype == PA_DTYPE_F32 ? 1 : 0;
+  // Each call takes the next set of work-queue counters, so calls that overlap on one device
+  // (other streams) use different counters unless kQueueSlots of them are in flight at once.
+  static std::atomic<uint32_t> calls{0};
+  a.queue_slot = (int32_t)(calls.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
   const int qpi = prefill_queries_per_item(dtype, head_dim, a.gh_max);
   const size_t prefix_bytes = (size_t)((num_seqs + 1 + 3) & ~3) * sizeof(int32_t);
   hipError_t err;

@@ -107,6 +107,9 @@ struct StoreArgs {
   int32_t block_size;
 };
 
+// Sets of prefill work-queue counters; the host hands them to calls in turn.
+constexpr int kQueueSlots = 64;
+
 struct PrefillArgs {
   const void* q;                // [num_tokens][num_heads][head_dim], token stride q_token_stride
   const void* k_cache;
@@ -130,6 +133,7 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t out_f32;
   int32_t num_waves;
+  int32_t queue_slot;           // which set of work-queue counters this call uses (< kQueueSlots)
 };
 
 // Launchers (return the launch error, hipSuccess otherwise).

@@ -442,14 +442,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int s, int g,
   }
 }
 
-// Workgroups are dealt round-robin to the 8 XCDs; renumbered this way, consecutive numbers
-// (which take consecutive work items) run on one XCD and share its L2.
-__device__ __forceinline__ int xcd_group() {
-  int grp = blockIdx.x;
-  if ((gridDim.x & 7) == 0) grp = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  return grp;
-}
-
 // s_prefix[i] = first work item of sequence i, where a sequence has ceil(n / queries_per_item)
 // items per (kv head, head group); n = its new tokens. Returns the total. All threads call it.
 __device__ int build_item_prefix(const PrefillArgs& a, int queries_per_item, int32_t* s_prefix, int32_t* s_wsum) {
@@ -489,6 +481,50 @@ __device__ int build_item_prefix(const PrefillArgs& a, int queries_per_item, int
   return s_prefix[a.num_seqs];
 }
 
+// Work queues. Items cost from one 32-key step to thousands (a query block's keys run up to its
+// last query), so a fixed assignment of items to persistent workgroups leaves some with far more
+// work than others: round-robin over the items in their order gives the busiest 1.25-1.5 times
+// the mean on long and mixed prompts. Instead each workgroup takes its next item (per-wavefront
+// kernel: the next chunk of four, one per wavefront) from a counter when it is free; its first
+// one is fixed, so no launch starts by waiting on an atomic. There is one counter per XCD
+// (workgroups are dealt to the 8 XCDs round-robin), and the items are dealt to them in chunks of
+// kQueueChunk consecutive ones, neighbouring query blocks of one (sequence, kv head) that read
+// the same K/V pages, so those stay in one XCD's L2.
+// The counters live in a static array, kQueueSlots sets of them; the host gives every call the
+// next set. The last wavefront or workgroup of a launch to finish sets its counters back to zero,
+// so every launch (and every replay of a captured one) starts from zero. Nothing waits on another
+// workgroup: a launch whose workgroups run one after another is only slower.
+constexpr int kQueueChunk = 4;
+constexpr int kQueueWords = 16;  // 8 XCD counters, the finished count, padding
+__device__ uint32_t g_prefill_queues[kQueueSlots * kQueueWords];
+
+struct WorkQueue {
+  uint32_t* ctr;
+  int nq, q;
+  uint32_t rank, per_queue;  // this workgroup's index among its queue's workgroups, and their count
+  __device__ WorkQueue(const PrefillArgs& a) {
+    ctr = g_prefill_queues + (uint32_t)a.queue_slot * kQueueWords;
+    nq = (gridDim.x & 7) == 0 ? 8 : 1;
+    q = (int)(blockIdx.x & (uint32_t)(nq - 1));
+    rank = blockIdx.x / (uint32_t)nq;
+    per_queue = gridDim.x / (uint32_t)nq;
+  }
+  // A workgroup's first index is its rank; later ones come from the counter, past the first
+  // round. Requests the next index (one lane's atomic; its value is read later).
+  __device__ uint32_t request(bool leader) const { return leader ? atomicAdd(ctr + q, 1u) + per_queue : 0u; }
+  // The item of index j of this queue: chunks of consecutive items, dealt to the queues in turn.
+  __device__ int item_of(uint32_t j) const {
+    const uint32_t c = j / kQueueChunk;
+    return (int)((c * (uint32_t)nq + (uint32_t)q) * kQueueChunk + j % kQueueChunk);
+  }
+  // Called once by each of the launch's `workers` after its last request; the last one resets.
+  __device__ void finish(bool leader, uint32_t workers) const {
+    if (leader && atomicAdd(ctr + 8, 1u) == workers - 1) {
+      for (int i = 0; i < 9; ++i) atomicExch(ctr + i, 0u);
+    }
+  }
+};
+
 template <int DT, int D>
 __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillArgs a) {
   extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]: first work item of each sequence
@@ -496,13 +532,27 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
   constexpr int NC = PrefillCfg<DT, D>::kNC;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = xcd_group() * kWavesPerGroup + __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb_queries = NC * (kHeadsPerTile / a.gh_max);
   const int H = a.num_kv_heads * a.n_hg;
 
   const int total = build_item_prefix(a, qb_queries, s_prefix, s_wsum);
 
-  for (int item = wave; item < total; item += a.num_waves) {
+  // The workgroup takes chunks of kQueueChunk (= its four wavefronts) consecutive items from its
+  // XCD's queue, one item per wavefront: neighbouring query blocks of one (sequence, kv head),
+  // which stream the same K/V pages on one CU. The next chunk is requested while this one runs;
+  // its index goes through LDS, double-buffered so that one barrier per chunk suffices.
+  static_assert(kQueueChunk == kWavesPerGroup, "one item of a chunk per wavefront");
+  __shared__ uint32_t s_next[2];
+  const WorkQueue wq(a);
+  const bool leader = tid == 0;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t j = wq.rank;
+  for (int k = 0;; ++k) {
+    const int first = wq.item_of(kQueueChunk * j);
+    if (first >= total) break;
+    const uint32_t jv = wq.request(leader);
+    const int item = first + wv;
+    if (item < total) {
     int lo = 0, hi = a.num_seqs;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -517,7 +567,13 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
     const int r = local / nqb;
     const int qb = nqb - 1 - (local - r * nqb);
     prefill_item<DT, D>(a, s, r / a.n_hg, r % a.n_hg, qb, lane);
+    }
+    // Slot k & 1 was last read in chunk k - 1, before the previous barrier.
+    if (leader) s_next[k & 1] = jv;
+    __syncthreads();
+    j = __builtin_amdgcn_readfirstlane(s_next[k & 1]);
   }
+  wq.finish(leader, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -859,17 +915,26 @@ template <int DT, int D>
 __global__ __launch_bounds__(kDecodeThreads) void prefill_shared_kernel(const PrefillArgs a) {
   extern __shared__ __align__(16) int32_t s_dyn[];
   __shared__ int32_t s_wsum[kWavesPerGroup];
+  __shared__ uint32_t s_next;
   constexpr int NC = SharedCfg<DT, D>::kNC;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = xcd_group();
   const int wg_queries = kWavesPerGroup * NC * (kHeadsPerTile / a.gh_max);
   const int H = a.num_kv_heads * a.n_hg;
   int32_t* s_prefix = s_dyn;
   char* bufs = reinterpret_cast<char*>(s_dyn + ((a.num_seqs + 1 + 3) & ~3));
   const int total = build_item_prefix(a, wg_queries, s_prefix, s_wsum);
-  for (int item = grp; item < total; item += gridDim.x) {
+  // Items from this XCD's queue: thread 0 requests the next index while the current item runs
+  // and leaves it in LDS before the item's last barrier.
+  const WorkQueue wq(a);
+  const bool leader = tid == 0;
+  if (leader) s_next = wq.rank;
+  __syncthreads();
+  for (;;) {
+    const int item = wq.item_of((uint32_t)__builtin_amdgcn_readfirstlane(s_next));
+    if (item >= total) break;
+    const uint32_t jv = wq.request(leader);
     int lo = 0, hi = a.num_seqs;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -882,9 +947,12 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_shared_kernel(const Pr
     const int qbg = __builtin_amdgcn_readfirstlane(nqb - 1 - (local - r * nqb));
     const int rr = __builtin_amdgcn_readfirstlane(r);
     prefill_shared_item<DT, D>(a, s, rr / a.n_hg, rr % a.n_hg, qbg, wv, lane, bufs);
-    // The next item's first store goes to buffer 0, which this item may have read last.
+    // Every wavefront has read s_next (above); the barrier after this store publishes the next
+    // index, and the next item's first store goes to buffer 0, which this item may have read last.
+    if (leader) s_next = jv;
     __syncthreads();
   }
+  wq.finish(leader, gridDim.x);
 }
 
 template <int DT, int D>

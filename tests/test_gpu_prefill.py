@@ -145,6 +145,57 @@ def test_prefill_with_large_logits(cuda, dt, d):
     assert (err <= TOL[dt]).all(), err.max()
 
 
+@pytest.mark.parametrize("dt,hq,d", [("bf16", 16, 128), ("fp16", 32, 64)])
+def test_prefill_repeats_and_graph_replays_are_bit_identical(cuda, dt, hq, d):
+    """Both prefill kernels take their work items from counters that every launch sets back to zero
+    when it ends, and each call takes the next of 64 counter sets. With more items than resident
+    workgroups (so most come from the counters), 70 calls in a row and four replays of a captured
+    call, each into a NaN-filled output with eager work between, give the same bits as the first
+    call, which matches the oracle on its short sequences (a skipped item would leave NaN)."""
+    import torch
+    import paged_attention_decode_amd as pa
+    lens = (2000, 1500, 1000, 700, 33, 1)
+    x = make_inputs(custom_config(dtype=dt, batch=len(lens), hq=hq, hkv=8, d=d, lens=lens, seed=808))
+    rng = np.random.default_rng(808)
+    qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = to_storage(rng.standard_normal((int(qs[-1]), hq, d), dtype=np.float32), dt)
+    dev = to_device(x, cuda)
+    qd = np_to_torch(q, dt).to(cuda)
+    qsd = torch.from_numpy(qs).to(cuda)
+    out = torch.empty((int(qs[-1]), hq, d), dtype=torch.float32, device=cuda)
+
+    def call():
+        pa.paged_prefill(qd, dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"], qsd, x.scale,
+                         out)
+
+    out.fill_(float("nan"))
+    call()
+    torch.cuda.synchronize()
+    first = out.cpu().numpy().copy()
+    assert np.isfinite(first).all()
+    short = [3, 4, 5]
+    ref = oracle.prefill(q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, qs, x.scale, geometry(x),
+                         seqs=short)
+    for s_ in short:
+        rows = slice(qs[s_], qs[s_ + 1])
+        assert np.abs(first[rows] - ref[rows]).max() <= TOL[dt], s_
+    for i in range(70):
+        out.fill_(float("nan"))
+        call()
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes() == first.tobytes(), f"call {i}"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes() == first.tobytes(), f"replay {rep}"
+    print(f"[gpu] prefill repeats and replays, {dt} head_dim {d}: bit-identical", flush=True)
+
+
 def test_store_then_prefill_then_decode_chain(cuda):
     """A prompt stored and prefilled, then one decode step: both against the oracle."""
     import torch
