@@ -196,6 +196,33 @@ def test_prefill_repeats_and_graph_replays_are_bit_identical(cuda, dt, hq, d):
     print(f"[gpu] prefill repeats and replays, {dt} head_dim {d}: bit-identical", flush=True)
 
 
+def test_prefill_without_items_leaves_out_and_its_counters_clean(cuda):
+    """Every context empty (no work items): 65 launches, enough to use every one of the 64 counter
+    sets, leave out untouched and their counters at zero, so a real call afterwards on a recycled
+    set matches the oracle."""
+    import torch
+    import paged_attention_decode_amd as pa
+    dt, hq, hkv, d = "bf16", 8, 2, 128
+    lens = (300, 120, 45)
+    x = make_inputs(custom_config(dtype=dt, batch=len(lens), hq=hq, hkv=hkv, d=d, lens=lens, seed=909))
+    rng = np.random.default_rng(909)
+    qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = to_storage(rng.standard_normal((int(qs[-1]), hq, d), dtype=np.float32), dt)
+    dev = to_device(x, cuda)
+    qd = np_to_torch(q, dt).to(cuda)
+    qsd = torch.from_numpy(qs).to(cuda)
+    zero_lens = torch.zeros_like(dev["context_lens"])
+    out = torch.full((int(qs[-1]), hq, d), float("nan"), dtype=torch.float32, device=cuda)
+    for _ in range(65):
+        pa.paged_prefill(qd, dev["k_cache"], dev["v_cache"], dev["block_tables"], zero_lens, qsd, x.scale, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    pa.paged_prefill(qd, dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"], qsd, x.scale, out)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, qs, x.scale, geometry(x))
+    assert np.abs(out.cpu().numpy() - ref).max() <= TOL[dt]
+
+
 def test_store_then_prefill_then_decode_chain(cuda):
     """A prompt stored and prefilled, then one decode step: both against the oracle."""
     import torch
