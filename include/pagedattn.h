@@ -326,8 +326,8 @@ int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t 
  *   Other arguments and limits as for pa_paged_attention_decode.
  * Workgroups take their work items from counters in a small fixed array of the library (no
  * allocation; every launch leaves its counters at zero when it ends, so calls can be recorded
- * into a HIP graph). Calls take the 64 sets of counters in turn: calls that run at the same time
- * on one device (other streams, or replays of captured calls) must not number 64 or more, or two
+ * into a HIP graph). Calls take the 1024 sets of counters in turn: calls that run at the same time
+ * on one device (other streams, or replays of captured calls) must not number 1024 or more, or two
  * of them may share counters and skip work.
  */
 int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache, const void* v_cache,

@@ -108,7 +108,7 @@ struct StoreArgs {
 };
 
 // Sets of prefill work-queue counters; the host hands them to calls in turn.
-constexpr int kQueueSlots = 64;
+constexpr int kQueueSlots = 1024;
 
 struct PrefillArgs {
   const void* q;                // [num_tokens][num_heads][head_dim], token stride q_token_stride
