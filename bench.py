@@ -775,7 +775,9 @@ def measure_prefill(workload: str, steps: int, warmup: int) -> dict:
         "config": dict(describe(cfg), prompt_tokens=int(qs[-1]), useful_flops=flops),
         "tokens_per_s": round(float(qs[-1]) / (ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None, "kernel": "prefill_kernel",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": ("prefill_shared_kernel (workgroup-shared K/V)"
+                                if cfg.dtype != "fp32" and cfg.head_dim == 128 else "prefill_kernel (per wavefront)"),
                      "kernel_mean_ms": round(ms, 5), "mfma_ceiling": ceiling}}
 
 
