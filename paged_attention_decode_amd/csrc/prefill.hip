@@ -34,6 +34,13 @@
 // V of the next step as soon as this step's second product is issued. Every
 // query block of a sequence re-reads the same keys, so the loads use the
 // default (caching) policy.
+//
+// Two kernels share this scheme. prefill_kernel gives each wavefront its own
+// item and its own K/V loads. prefill_shared_kernel (16-bit inputs at
+// head_dim 128) gives a workgroup four consecutive query blocks; each 32-key
+// step is loaded once per workgroup, a quarter by each wavefront, and read by
+// all four from LDS. Both take their items from per-XCD work queues
+// (WorkQueue below), so no workgroup ends with much more work than the others.
 
 #include "device_common.h"
 
@@ -491,7 +498,7 @@ __device__ int build_item_prefix(const PrefillArgs& a, int queries_per_item, int
 // kQueueChunk consecutive ones, neighbouring query blocks of one (sequence, kv head) that read
 // the same K/V pages, so those stay in one XCD's L2.
 // The counters live in a static array, kQueueSlots sets of them; the host gives every call the
-// next set. The last wavefront or workgroup of a launch to finish sets its counters back to zero,
+// next set. The last workgroup of a launch to finish sets its counters back to zero,
 // so every launch (and every replay of a captured one) starts from zero. Nothing waits on another
 // workgroup: a launch whose workgroups run one after another is only slower.
 constexpr int kQueueChunk = 4;
@@ -553,20 +560,20 @@ __global__ __launch_bounds__(kDecodeThreads) void prefill_kernel(const PrefillAr
     const uint32_t jv = wq.request(leader);
     const int item = first + wv;
     if (item < total) {
-    int lo = 0, hi = a.num_seqs;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_prefix[mid] <= item) lo = mid; else hi = mid;
-    }
-    const int s = lo;
-    const int local = item - s_prefix[s];
-    // Within a sequence, the query blocks of one (kv head, head group) are consecutive items,
-    // so neighbouring waves stream the same K/V pages at about the same time. Later query
-    // blocks (longer key ranges) come first.
-    const int nqb = (s_prefix[s + 1] - s_prefix[s]) / H;
-    const int r = local / nqb;
-    const int qb = nqb - 1 - (local - r * nqb);
-    prefill_item<DT, D>(a, s, r / a.n_hg, r % a.n_hg, qb, lane);
+      int lo = 0, hi = a.num_seqs;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_prefix[mid] <= item) lo = mid; else hi = mid;
+      }
+      const int s = lo;
+      const int local = item - s_prefix[s];
+      // Within a sequence, the query blocks of one (kv head, head group) are consecutive items,
+      // so neighbouring waves stream the same K/V pages at about the same time. Later query
+      // blocks (longer key ranges) come first.
+      const int nqb = (s_prefix[s + 1] - s_prefix[s]) / H;
+      const int r = local / nqb;
+      const int qb = nqb - 1 - (local - r * nqb);
+      prefill_item<DT, D>(a, s, r / a.n_hg, r % a.n_hg, qb, lane);
     }
     // Slot k & 1 was last read in chunk k - 1, before the previous barrier.
     if (leader) s_next[k & 1] = jv;
