@@ -198,6 +198,51 @@ def test_prefill_repeats_and_graph_replays_are_bit_identical(cuda, dt, hq, d):
     print(f"[gpu] prefill repeats and replays, {dt} head_dim {d}: bit-identical", flush=True)
 
 
+def test_prefill_calls_overlapping_on_two_streams(cuda):
+    """Calls that run at the same time on one device take different counter sets. Two prefills with
+    fewer workgroups than the device holds (so both can be resident together), one for each kernel
+    (bf16 head_dim 128: workgroup-shared; fp16 head_dim 64: per wavefront), are launched 16 times
+    each, alternating between two streams, into NaN-filled outputs of their own. Every output
+    must have the bits of the same prefill run alone, which matches the oracle on its short
+    sequences."""
+    import torch
+    import paged_attention_decode_amd as pa
+    lens = (2000, 1500, 40, 1)
+    short = [2, 3]
+    probs = []
+    for dt, d, seed in (("bf16", 128, 811), ("fp16", 64, 812)):
+        x = make_inputs(custom_config(dtype=dt, batch=len(lens), hq=8, hkv=2, d=d, lens=lens, seed=seed))
+        rng = np.random.default_rng(seed)
+        qs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        q = to_storage(rng.standard_normal((int(qs[-1]), 8, d), dtype=np.float32), dt)
+        dev = to_device(x, cuda)
+        args = (np_to_torch(q, dt).to(cuda), dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                dev["context_lens"], torch.from_numpy(qs).to(cuda), x.scale)
+        alone = torch.full((int(qs[-1]), 8, d), float("nan"), dtype=torch.float32, device=cuda)
+        pa.paged_prefill(*args, alone)
+        torch.cuda.synchronize()
+        got = alone.cpu().numpy()
+        assert np.isfinite(got).all(), dt
+        ref = oracle.prefill(q, x.k_cache, x.v_cache, x.block_tables, x.context_lens, qs, x.scale, geometry(x),
+                             seqs=short)
+        for s_ in short:
+            rows = slice(qs[s_], qs[s_ + 1])
+            assert np.abs(got[rows] - ref[rows]).max() <= TOL[dt], (dt, s_)
+        outs = [torch.full_like(alone, float("nan")) for _ in range(16)]
+        probs.append((dt, args, alone, outs))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for i in range(16):
+        for (dt, args, alone, outs), st in zip(probs, streams):
+            with torch.cuda.stream(st):
+                pa.paged_prefill(*args, outs[i])
+    torch.cuda.synchronize()
+    for dt, args, alone, outs in probs:
+        for i, o in enumerate(outs):
+            assert torch.equal(o.view(torch.int32), alone.view(torch.int32)), (dt, i)
+    print("[gpu] prefill on two streams at once: every call bit-identical to a call alone", flush=True)
+
+
 def test_prefill_without_items_leaves_out_and_its_counters_clean(cuda):
     """Every context empty (no work items): 1025 launches, enough to use every one of the 1024
     counter sets, leave out untouched and their counters at zero, so a real call afterwards on a
