@@ -327,8 +327,10 @@ int pa_decode_step(const void* q, const void* k_new, const void* v_new, int64_t 
  * Workgroups take their work items from counters in a small fixed array of the library (no
  * allocation; every launch leaves its counters at zero when it ends, so calls can be recorded
  * into a HIP graph). Calls take the 1024 sets of counters in turn: calls that run at the same time
- * on one device (other streams, or replays of captured calls) must not number 1024 or more, or two
- * of them may share counters and skip work.
+ * on one device (other streams, other host threads) must not number 1024 or more, or two of them
+ * may share counters and skip work. A captured call keeps the set it took at capture. Replays of
+ * one executable graph are ordered and never overlap, but two executable graphs instantiated
+ * from one capture share that set: the caller must not run them at the same time.
  */
 int pa_paged_prefill(const void* q, int64_t q_token_stride, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
