@@ -127,8 +127,10 @@ int pa_store_kvcache(const void* k, const void* v, const int32_t* slot_mapping,
  *                 contiguous, consecutive sequences q_seq_stride ELEMENTS apart
  *                 (>= num_heads * head_dim).
  *   k_cache, v_cache  num_blocks blocks in the layout above, `dtype`.
- *   block_tables  [num_seqs][max_blocks_per_seq] int32, contiguous. Entries
- *                 past ceil(L_s / block_size) are never read. An entry outside
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32, contiguous; the whole
+ *                 table must be readable. Entries past ceil(L_s / block_size)
+ *                 never affect the result (the kernel may read them to warm
+ *                 its cache, but never uses their values). An entry outside
  *                 [0, num_blocks) is clamped into range (unspecified output).
  *   context_lens  [num_seqs] int32, L_s. Values are clamped to
  *                 [0, max_blocks_per_seq * block_size]. L_s == 0 gives zeros.

@@ -488,6 +488,21 @@ struct Piece {
 
 // SHARED: the call reads shared prefixes (split modes only); a separate instance keeps that
 // bookkeeping out of the plain kernel's walk over its ranges.
+// Context length of sequence s, read together with the first lines of its block-table row.
+// Entries 0, 16 and 31 (clamped to the row) are read only to bring their lines into the scalar
+// cache, so the segment's first block-table reads hit there instead of going to memory after
+// the context length has arrived: two dependent memory round trips at a segment's start become
+// one. An empty asm statement after the length's clamp consumes them, which keeps the reads and
+// places their wait beside the length's own.
+__device__ __forceinline__ int seq_len_and_table_lines(const DecodeArgs& a, int s, int max_len) {
+  const_i32* row = (const_i32*)(a.block_tables + (int64_t)s * a.max_blocks);
+  const int last = a.max_blocks - 1;
+  const int b0 = row[0], b1 = row[min(16, last)], b2 = row[min(31, last)];
+  const int L = clamp_len(a.context_lens[s], max_len);
+  asm volatile("" ::"s"(b0), "s"(b1), "s"(b2));
+  return L;
+}
+
 template <int DT, int D, bool FUSE, bool SHARED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   // Split modes: [num_seqs + 1], the first global tile of each sequence. Workgroup split: the
@@ -525,7 +540,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     for (int seg = first; seg < nseg; seg += gridDim.x) {
       const int s = seg / H;
       const int r = seg - s * H;
-      const int L = clamp_len(a.context_lens[s], max_len);
+      const int L = seq_len_and_table_lines(a, s, max_len);
       const int tiles = max(1, (L + kTile - 1) / kTile);
       const int parts = min(kWavesPerGroup, tiles);
       if (parts == 1) {
@@ -575,7 +590,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     for (int seg = wave; seg < nseg; seg += a.num_waves) {
       const int s = seg / H;
       const int r = seg - s * H;
-      const int L = clamp_len(a.context_lens[s], max_len);
+      const int L = seq_len_and_table_lines(a, s, max_len);
       const int tiles = max(1, (L + kTile - 1) / kTile);
       Piece<DT, D, FUSE>::run(a, s, r, L, 0, tiles, true, 0, lane);
     }
