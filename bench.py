@@ -58,6 +58,7 @@ WORKLOAD_PARTITION = {"long_ctx_bf16": 512}
 ONE_THREAD_BASELINE = {"tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"}
 # Default run: full-prompt prefill records (TFLOP/s) of these workloads' prompts.
 PREFILL_RECORDS = ("llama32_1b_fp16", "skewed_prefix_bf16")
+PREFILL_RECORD_STEPS, PREFILL_RECORD_WARMUP = 100, 10
 KERNEL_SOURCE = ROOT / "paged_attention_decode_amd" / "csrc" / "decode.hip"
 PROFILES = ROOT / "profiles"
 COPY_BYTES = 256 << 20
@@ -1197,11 +1198,13 @@ def main():
         result["stream_read_ceiling"] = ceiling
     if records:
         result["workloads"] = records
-        # The next row's kernel (paged prefill), on the prompts of two workloads.
+        # The next row's kernel (paged prefill), on the prompts of two workloads. The same step
+        # counts as a --prefill run: with fewer warm-up launches after the host-side input
+        # generation, the first timed launches run slower and the record understates the kernel.
         prefill = {}
         for name in PREFILL_RECORDS:
             print(f"[bench] prefill record {name}", file=sys.stderr, flush=True)
-            r = measure_prefill(name, 10, 2)
+            r = measure_prefill(name, PREFILL_RECORD_STEPS, PREFILL_RECORD_WARMUP)
             prefill[name] = {"value": r["value"], "unit": r["unit"], "dtype": r["dtype"],
                              "ms_per_step": r["roofline"]["kernel_mean_ms"],
                              "prompt_tokens": r["config"]["prompt_tokens"], "roofline": r["roofline"]}
