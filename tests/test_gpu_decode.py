@@ -254,16 +254,25 @@ def test_identical_keys_give_mean_of_values(cuda):
 
 
 def test_poisoned_tail_slots_and_unused_blocks_change_nothing(cuda):
-    """NaN in slots past each context and in unreferenced blocks must not reach the output."""
+    """NaN in slots past each context and in unreferenced blocks, and garbage block-table entries
+    past each context's last block (the kernel may read them, never use them), must not reach the
+    output."""
     cfg = custom_config(dtype="bf16", batch=5, hq=8, hkv=2, lens=(3, 17, 250, 33, 1), seed=5)
     x = make_inputs(cfg)
     x.slot_mapping[:] = -1
     geo = geometry(x)
-    clean = {p: _run_step(to_device(x, cuda), x, partition_size=p).cpu().numpy() for p in (-2, -1, 0, 16)}
+    modes = (-3, -2, -1, 0, 16)
+    clean = {p: _run_step(to_device(x, cuda), x, partition_size=p).cpu().numpy() for p in modes}
+    bs = cfg.block_size
+    junk = np.array([-1, -(2 ** 31), 2 ** 31 - 1, x.num_blocks, 7 * x.num_blocks + 3], np.int64)
+    for s in range(cfg.batch):
+        used = (int(x.context_lens[s]) + bs - 1) // bs
+        tail_entries = x.block_tables.shape[1] - used
+        x.block_tables[s, used:] = np.resize(junk, tail_entries).astype(np.int32)
+    assert (x.block_tables < 0).any(), "some sequence must have table entries past its context"
     kp = poison_blocks(x.k_cache, x.unused_blocks, cfg)
     vp = poison_blocks(x.v_cache, x.unused_blocks, cfg)
     # tail slots of each sequence's last block, written with NaN rows by the oracle's scatter
-    bs = cfg.block_size
     tail = []
     for s in range(cfg.batch):
         L = int(x.context_lens[s])
