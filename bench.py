@@ -986,6 +986,25 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
             "kernel_mean_ms": round(am, 5), "achieved": round(roof_bytes / (am * 1e-3) / 1e9, 2),
             "frac": round(roof_bytes / (am * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "the library's own choice for this batch (0 = automatic), cold, attention kernel only"}
+    if not args.fused_step and not args.graph and not args.no_extra_timings:
+        # The library's fused step (pa_decode_step: the scatter done inside the attention launch)
+        # on the same inputs, timed as `value` is: a warm loop of K steps, wall clock around them.
+        # It writes the same bits to the same slots, so the inputs are unchanged afterwards.
+        def fused():
+            pa.decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, x.scale, out,
+                           partition_size=psize, cached_prefix_tokens=args.cached_prefix_tokens,
+                           shared_prefix=args.shared_prefix)
+        for _ in range(max(1, args.warmup)):
+            fused()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            fused()
+        torch.cuda.synchronize()
+        fms = (time.perf_counter() - t0) * 1e3 / K
+        rec["fused_step"] = {"ms_per_step": round(fms, 5), "value": round(kv_bytes / (fms * 1e-3) / 1e9, 2),
+                             "tokens_per_s": round(cfg.batch / (fms * 1e-3), 1),
+                             "note": "pa_decode_step, warm loop of the same step count, wall clock (as value)"}
     if headline and not args.no_extra_timings:
         calls = {"store": store, "decode": decode, "store_plus_decode": step}
         for pz, nm in ((-2, "decode_balanced"), (-1, "decode_one_pass"), (512, "decode_split_512")):
@@ -1191,7 +1210,7 @@ def main():
         "pct_hbm_peak": round(100.0 * head["value"] / HBM_PEAK_GBS, 2),
         "roofline": head["roofline"],
     }
-    for key in ("cold_step", "split_cold_median_us", "timings", "comparators", "cpu_baseline"):
+    for key in ("cold_step", "split_cold_median_us", "fused_step", "timings", "comparators", "cpu_baseline"):
         if key in head:
             result[key] = head[key]
     if ceiling:
