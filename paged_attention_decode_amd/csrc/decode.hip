@@ -486,8 +486,6 @@ struct Piece {
 #define PA_XCD_REMAP 1
 #endif
 
-// SHARED: the call reads shared prefixes (split modes only); a separate instance keeps that
-// bookkeeping out of the plain kernel's walk over its ranges.
 // Context length of sequence s, read together with the first lines of its block-table row.
 // Entries 0, 16 and 31 (clamped to the row) are read only to bring their lines into the scalar
 // cache, so the segment's first block-table reads hit there instead of going to memory after
@@ -503,6 +501,8 @@ __device__ __forceinline__ int seq_len_and_table_lines(const DecodeArgs& a, int 
   return L;
 }
 
+// SHARED: the call reads shared prefixes (split modes only); a separate instance keeps that
+// bookkeeping out of the plain kernel's walk over its ranges.
 template <int DT, int D, bool FUSE, bool SHARED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   // Split modes: [num_seqs + 1], the first global tile of each sequence. Workgroup split: the
