@@ -178,9 +178,10 @@ def kernel_source_sha(kernel: str = "decode") -> str:
     return hashlib.sha256(src.read_bytes()).hexdigest()
 
 
-def profile_name(workload: str, shared_prefix: bool = False) -> str:
-    """Workload part of a profile file name (runs with the shared-prefix option are kept apart)."""
-    return workload + ("_shared_prefix" if shared_prefix else "")
+def profile_name(workload: str, shared_prefix: bool = False, fused_step: bool = False) -> str:
+    """Workload part of a profile file name (runs with the shared-prefix option or the fused step
+    are kept apart)."""
+    return workload + ("_shared_prefix" if shared_prefix else "") + ("_fused_step" if fused_step else "")
 
 
 def traffic_from_profiles(workload: str, launches_bytes: float):
@@ -400,13 +401,13 @@ def summarize_graph_trace(workload: str, directory: str, command: str, layers: i
 
 
 def summarize_trace(workload: str, directory: str, command: str, kernel: str = "decode",
-                    shared_prefix: bool = False) -> Path:
+                    shared_prefix: bool = False, fused_step: bool = False) -> Path:
     """Per-kernel duration statistics of a rocprofv3 --kernel-trace --stats run, as text."""
     import csv
     files = sorted(Path(directory).rglob("*kernel_stats.csv"))
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {directory}")
-    opt = " --shared-prefix" if shared_prefix else ""
+    opt = (" --shared-prefix" if shared_prefix else "") + (" --fused-step" if fused_step else "")
     lines = [f"# rocprofv3 kernel statistics, workload {workload}{opt}",
              f"# command: {command}",
              f"# summary command: python bench.py --workload {workload}{opt} "
@@ -432,7 +433,7 @@ def summarize_trace(workload: str, directory: str, command: str, kernel: str = "
         if timed:
             lines.append(f"timed_launches: {len(timed)} (the last --steps launches of the {main_name} kernel)")
             lines.append(f"timed_launches_mean_us: {sum(timed) / len(timed) / 1e3:.2f}")
-    path = PROFILES / f"{kernel}_{profile_name(workload, shared_prefix)}_kernel_trace.txt"
+    path = PROFILES / f"{kernel}_{profile_name(workload, shared_prefix, fused_step)}_kernel_trace.txt"
     PROFILES.mkdir(exist_ok=True)
     path.write_text("\n".join(lines) + "\n")
     return path
@@ -958,7 +959,7 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
                                             float(np.median(cold_kernel_ms))) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles(profile_name(name, args.shared_prefix), kv_bytes),
+                     "traffic": traffic_from_profiles(profile_name(name, args.shared_prefix, args.fused_step), kv_bytes),
                      "bytes": "distinct K/V bytes (shared blocks once)" if args.shared_prefix else "logical K/V bytes",
                      "algorithmic_bytes_per_launch": roof_bytes,
                      "kernel": "decode_kernel (attention; excludes store and merge; with the shared-prefix option "
@@ -1162,7 +1163,7 @@ def main():
         return
     if args.summarize_trace:
         print(summarize_trace(workload, args.summarize_trace, args.trace_command,
-                              "prefill" if args.prefill else "decode", args.shared_prefix))
+                              "prefill" if args.prefill else "decode", args.shared_prefix, args.fused_step))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
