@@ -54,6 +54,10 @@ DEFAULT_WORKLOAD = "skewed_prefix_bf16"
 RECORD_WORKLOADS = ["tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16", "long_ctx_bf16"]
 # Launch mode a workload is specified with (others: 0, the library's automatic choice).
 WORKLOAD_PARTITION = {"long_ctx_bf16": 512}
+# Prefix-cache hit length a workload is specified with: the leading tokens its sequences share
+# (groups of 8 share their first 512 in the skewed batch). It is passed as cached_prefix_tokens,
+# as an engine passes the hit length its block manager reports; others use the library default.
+WORKLOAD_CACHED_PREFIX = {"skewed_prefix_bf16": 512}
 # Workloads whose CPU baseline is also taken with one BLAS thread.
 ONE_THREAD_BASELINE = {"tiny_fp32", "qwen3_0p6b_bf16", "llama32_1b_fp16"}
 # Default run: full-prompt prefill records (TFLOP/s) of these workloads' prompts.
@@ -75,8 +79,9 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None,
                     help="0 automatic, -1 one pass, -2 balanced split, -3 workgroup split, >0 fixed ranges of "
                          "that many tokens (default: the workload's own, 512 for the long-context one, else 0)")
-    ap.add_argument("--cached-prefix-tokens", type=int, default=0,
-                    help="leading tokens per context read with cached loads (0 library default, -1 none)")
+    ap.add_argument("--cached-prefix-tokens", type=int, default=None,
+                    help="leading tokens per context read with cached loads (0 library default, -1 none; "
+                         "default: the workload's shared-prefix length, 512 for the skewed batch, else 0)")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="read the leading blocks that neighbouring sequences share once per group "
                          "(pa_decode_opts.shared_prefix; the sharing is found on the device)")
@@ -811,6 +816,7 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
 
     cfg = get_config(name)
     psize = args.partition_size if args.partition_size is not None else WORKLOAD_PARTITION.get(name, 0)
+    cpt = args.cached_prefix_tokens if args.cached_prefix_tokens is not None else WORKLOAD_CACHED_PREFIX.get(name, 0)
     print(f"[bench] {name}: generating", file=sys.stderr, flush=True)
     x = make_inputs(cfg)
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
@@ -828,15 +834,15 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
     def store():
         pa.store_kvcache(k_new, v_new, slots, k_cache, v_cache)
 
-    def decode(events=None, psz=psize, shared=args.shared_prefix):
+    def decode(events=None, psz=psize, shared=args.shared_prefix, cpt_=cpt):
         pa.paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, x.scale, out,
-                                  partition_size=psz, cached_prefix_tokens=args.cached_prefix_tokens,
+                                  partition_size=psz, cached_prefix_tokens=cpt_,
                                   events=events, shared_prefix=shared)
 
     def step(events=None):
         if args.fused_step:
             pa.decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, x.scale, out,
-                           partition_size=psize, cached_prefix_tokens=args.cached_prefix_tokens,
+                           partition_size=psize, cached_prefix_tokens=cpt,
                            events=events, shared_prefix=args.shared_prefix)
             return
         store()
@@ -923,6 +929,17 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
         torch.cuda.synchronize()
         auto_cold_ms = [b.elapsed_time(e) for b, e in evs]
 
+    # A workload specified with its shared-prefix length is also timed, cold, with the library's
+    # default cache policy.
+    default_policy_cold_ms = None
+    if cpt != 0 and not args.no_extra_timings:
+        evs = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+        for e in evs:
+            sr.flush()
+            decode(e, psize, args.shared_prefix, 0)
+        torch.cuda.synchronize()
+        default_policy_cold_ms = [b.elapsed_time(e) for b, e in evs]
+
     ms_per_step = wall * 1e3 / K
     kv_bytes = x.kv_bytes
     # With shared prefixes the kernel reads each shared block once: its algorithmic bytes are the
@@ -940,7 +957,7 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
         "config": dict(describe(cfg), kv_bytes_per_step=kv_bytes, unique_kv_bytes=x.unique_kv_bytes,
                        partition_size=psize, plan_range_tokens=plan["range_tokens"],
                        merge_kernel=plan["uses_reduce"], shared_prefix=bool(args.shared_prefix),
-                       cached_prefix_tokens=args.cached_prefix_tokens or pa.DEFAULT_CACHED_PREFIX_TOKENS,
+                       cached_prefix_tokens=cpt or pa.DEFAULT_CACHED_PREFIX_TOKENS,
                        launch="hip graph replay" if args.graph else "eager",
                        step="pa_decode_step (fused scatter + attention)" if args.fused_step
                        else "pa_store_kvcache + pa_paged_attention_decode"),
@@ -987,13 +1004,21 @@ def measure_workload(name: str, args, dev, sr: "StreamRead", headline: bool) -> 
             "kernel_mean_ms": round(am, 5), "achieved": round(roof_bytes / (am * 1e-3) / 1e9, 2),
             "frac": round(roof_bytes / (am * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "the library's own choice for this batch (0 = automatic), cold, attention kernel only"}
+    if default_policy_cold_ms:
+        dm = float(np.mean(default_policy_cold_ms))
+        rec["roofline"]["library_default_cache_policy"] = {
+            "cached_prefix_tokens": pa.DEFAULT_CACHED_PREFIX_TOKENS, "kernel_mean_ms": round(dm, 5),
+            "achieved": round(roof_bytes / (dm * 1e-3) / 1e9, 2),
+            "frac": round(roof_bytes / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "the same launch with the library's default cache policy (no hit length passed), cold, "
+                    "attention kernel only"}
     if not args.fused_step and not args.graph and not args.no_extra_timings:
         # The library's fused step (pa_decode_step: the scatter done inside the attention launch)
         # on the same inputs, timed as `value` is: a warm loop of K steps, wall clock around them.
         # It writes the same bits to the same slots, so the inputs are unchanged afterwards.
         def fused():
             pa.decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, x.scale, out,
-                           partition_size=psize, cached_prefix_tokens=args.cached_prefix_tokens,
+                           partition_size=psize, cached_prefix_tokens=cpt,
                            shared_prefix=args.shared_prefix)
         for _ in range(max(1, args.warmup)):
             fused()
